@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the W8A8 block-scaled FP8 linear-layer hot path on one MI355X.
+
+Headline ("step"): one prefill-shaped linear layer, 4096 tokens x 7168 ->
+18432, i.e. fp8_act_quant (per token, per 128 channels, fp32 scales) on the
+bf16 activations followed by fp8_block_gemm against E4M3 weights with
+128x128 fp32 block scales, bf16 output.  Weights are quantised once,
+outside the timed region (offline in the method).  Inputs are seeded
+synthetic tensors already resident in HBM.
+
+value = 2*M*N*K / (time per step), i.e. block-scaled FP8 GEMM TFLOP/s
+including act_quant.
+
+The same JSON line carries
+  roofline      for the dominant kernel (the block GEMM), its average
+                launch duration measured with events on its stream;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same
+                workload (rank 0, one GPU only);
+  legs          the other rows of the hot path measured the same way:
+                decode-shaped GEMMs (M = 1, 8, 32, 128; K 8192 -> N 28672,
+                ue8m0 scales, weights rotated over two copies so the
+                256 MB last-level cache cannot serve them), the MXFP8 GEMM
+                (8192^3) and the grouped MoE GEMM (256 experts, 4096 tokens,
+                top-8, N 2048, K 7168), plus act_quant bandwidth.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-legs", action="store_true", help="time the headline step only")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
+    p.add_argument("--only", default="", help="run one leg only: decode|mx|moe|prefill")
+    return p.parse_args()
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(HERE, "fp8_block_scaled_02_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name, launches_per_record=1):
+    """HBM traffic of one launch from the committed rocprofv3 counter summary,
+    or None if it is missing or was taken on different kernel sources."""
+    path = os.path.join(HERE, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def timed(torch, fn, iters):
+    """Average device time of fn() over iters launches (events on the
+    current stream, which is where the library enqueues)."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(iters):
+        fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / iters * 1e-3
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fp8_block_scaled_02_amd as F
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    legs = {}
+
+    # ---- headline: prefill linear ------------------------------------------------
+    c = W.prefill_linear(device=dev)
+    M, K = c.x.shape
+    N = c.w.shape[0]
+    wq, ws = F.fp8_weight_quant(c.w, "fp32")
+    x = c.x
+    a = torch.empty(M, K, dtype=torch.uint8, device=dev)
+    sa = torch.empty(M, K // 128, dtype=torch.float32, device=dev)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        F.fp8_act_quant(x, 128, "fp32", q=a, scales=sa)
+        F.fp8_block_gemm(a, sa, wq, ws, torch.bfloat16, y=y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    flops = 2.0 * M * N * K
+    value = flops / (wall / args.steps) / 1e12
+
+    # per-kernel device times on the same stream
+    t_aq = timed(torch, lambda: F.fp8_act_quant(x, 128, "fp32", q=a, scales=sa), max(args.steps, 10))
+    t_gemm = timed(torch, lambda: F.fp8_block_gemm(a, sa, wq, ws, torch.bfloat16, y=y), max(args.steps, 10))
+    gemm_bytes = M * K + N * K + M * (K // 128) * 4 + (N // 128) * (K // 128) * 4 + M * N * 2
+    aq_bytes = M * K * 2 + M * K + M * (K // 128) * 4
+    achieved = flops / t_gemm / 1e12
+    traffic = load_traffic("block_gemm_prefill")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+                "kernel": "block_gemm_kernel", "avg_launch_us": round(t_gemm * 1e6, 2),
+                "algorithmic_bytes": gemm_bytes}
+    legs["prefill"] = {"act_quant_us": round(t_aq * 1e6, 2),
+                       "act_quant_GBps": round(aq_bytes / t_aq / 1e9, 1),
+                       "act_quant_hbm_frac": round(aq_bytes / t_aq / 1e9 / PEAK_HBM_GBS, 4),
+                       "gemm_us": round(t_gemm * 1e6, 2), "gemm_TFLOPs": round(achieved, 1)}
+    del c
+
+    # ---- CPU baseline: the oracle on a bounded sample -----------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle as O
+        xb = W.bits(x)
+        ow, osw = O.weight_quant(W.bits(W.prefill_linear(device=dev).w), 0)   # offline, untimed
+        rows = args.cpu_rows or 32
+        t0 = time.perf_counter()
+        oa, osa = O.act_quant(xb[:rows], 128, 0)
+        O.block_gemm(oa, osa, ow, osw)
+        t_cpu = time.perf_counter() - t0
+        if not args.cpu_rows and t_cpu < 8.0:      # grow the sample toward ~10-30 s
+            rows = int(min(M, max(rows, rows * 12.0 / max(t_cpu, 1e-3))))
+            t0 = time.perf_counter()
+            oa, osa = O.act_quant(xb[:rows], 128, 0)
+            O.block_gemm(oa, osa, ow, osw)
+            t_cpu = time.perf_counter() - t0
+        cpu = {"value": round(2.0 * rows * N * K / t_cpu / 1e12, 6), "unit": "TFLOP/s",
+               "cores": O.num_threads(), "kind": "oracle",
+               "sample": f"act_quant + block GEMM of the first {rows} of {M} token rows "
+                         f"(all {N} outputs, K {K}), {t_cpu:.1f} s"}
+        del ow, osw, xb
+
+    del x, a, sa, y, wq, ws
+    torch.cuda.empty_cache()
+
+    if not args.no_legs:
+        legs.update(run_legs(torch, F, W, dev, args.only))
+
+    out = {
+        "metric": "block-scaled FP8 GEMM TFLOPS (incl. act_quant) and % of MI355X FP8 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "pct_of_fp8_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
+        "config": {"workload": "prefill linear: act_quant (per token per 128, fp32 scales) + "
+                               "block-scaled FP8 GEMM (128x128 fp32 weight scales), bf16 out",
+                   "M": M, "K": K, "N": N},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "legs": legs,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_legs(torch, F, W, dev, only=""):
+    legs = {}
+    iters = 20
+    if only in ("", "decode"):
+        c = W.decode_linear(device=dev)
+        K, N = c.x.shape[1], c.w.shape[0]
+        copies = [F.fp8_weight_quant(c.w, "ue8m0") for _ in range(2)]   # > 256 MB together
+        del c.w
+        dec = {}
+        for M in (1, 8, 32, 128):
+            a, sa = F.fp8_act_quant(c.x[:M].contiguous(), 128, "ue8m0")
+            y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            st = [0]
+
+            def g():
+                wq, ws = copies[st[0] & 1]
+                st[0] += 1
+                F.fp8_block_gemm(a, sa, wq, ws, torch.bfloat16, y=y)
+            for _ in range(4):
+                g()
+            t = timed(torch, g, iters)
+            nbytes = N * K + (N // 128) * (K // 128) * 4 + M * K + M * (K // 128) * 4 + M * N * 2
+            dec[f"M{M}"] = {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+                            "hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
+                            "TFLOPs": round(2.0 * M * N * K / t / 1e12, 2)}
+        legs["decode"] = dec
+        del copies, c
+        torch.cuda.empty_cache()
+    if only in ("", "mx"):
+        A, B = W.mx_case(device=dev)
+        M, K = A.shape
+        N = B.shape[0]
+        qa, ea = F.fp8_act_quant(A, 32, "e8m0")
+        qb, eb = F.fp8_act_quant(B, 32, "e8m0")
+        y = torch.empty(M, N, dtype=torch.float32, device=dev)
+        t_q = timed(torch, lambda: F.fp8_act_quant(A, 32, "e8m0", q=qa, scales=ea), iters)
+        t = timed(torch, lambda: F.mxfp8_gemm(qa, ea, qb, eb, y=y), iters)
+        qbytes = M * K * 3 + M * K // 32
+        legs["mx"] = {"gemm_us": round(t * 1e6, 2), "TFLOPs": round(2.0 * M * N * K / t / 1e12, 1),
+                      "frac_fp8_peak": round(2.0 * M * N * K / t / 1e12 / PEAK_FP8_TFLOPS, 4),
+                      "act_quant32_us": round(t_q * 1e6, 2), "act_quant32_GBps": round(qbytes / t_q / 1e9, 1)}
+        del A, B, qa, ea, qb, eb, y
+        torch.cuda.empty_cache()
+    if only in ("", "moe"):
+        case = W.moe_case(device=dev)
+        E, N, K = case.w.shape
+        T = case.x.shape[0]
+        a, sa = F.fp8_act_quant(case.x, 128, "fp32")
+        wq = torch.empty(E, N, K, dtype=torch.uint8, device=dev)
+        ws = torch.empty(E, N // 128, K // 128, dtype=torch.float32, device=dev)
+        for e in range(E):
+            F.fp8_weight_quant(case.w[e], "fp32", q=wq[e], scales=ws[e])
+        del case.w
+        torch.cuda.empty_cache()
+        ri, offs = case.row_index.to(dev), case.offs.to(dev)
+        R = ri.shape[0]
+        y = torch.empty(R, N, dtype=torch.bfloat16, device=dev)
+        t = timed(torch, lambda: F.fp8_grouped_gemm(a, sa, ri, offs, wq, ws, torch.bfloat16, y=y), iters)
+        counts = (case.offs[1:] - case.offs[:-1])
+        active = int((counts > 0).sum())
+        nbytes = active * (N * K + (N // 128) * (K // 128) * 4) + T * (K + K // 128 * 4) + R * N * 2
+        legs["moe"] = {"us": round(t * 1e6, 2), "TFLOPs": round(2.0 * R * N * K / t / 1e12, 1),
+                       "GBps": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
+                       "active_experts": active, "max_rows": int(counts.max())}
+        del wq, ws, a, sa, y
+        torch.cuda.empty_cache()
+    return legs
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+"""Python binding of libfp8blk, the MI355X (gfx950) W8A8 block-scaled FP8
+linear-layer library.
+
+Argument marshalling only: every step of the hot path runs in the HIP
+kernels behind the C ABI declared in include/fp8blk.h.  torch provides the
+device memory and the stream (the current torch stream of the tensors'
+device).  The functions carry the C names (fp8_act_quant, fp8_weight_quant,
+fp8_block_gemm, mxfp8_gemm, fp8_grouped_gemm, fp8_cast_f32) and take torch
+tensors; outputs are allocated with torch when not supplied.
+
+There is no fallback: if libfp8blk.so is missing this module raises on
+first use.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8blk.so")
+
+# enums of include/fp8blk.h
+FP8B_OK = 0
+SCALE_FP32, SCALE_UE8M0, SCALE_E8M0_BYTE = 0, 1, 2
+OUT_F32, OUT_BF16 = 0, 1
+FMT_E4M3, FMT_E5M2 = 0, 1
+
+_SCALE_FMT = {"fp32": SCALE_FP32, "ue8m0": SCALE_UE8M0, "e8m0": SCALE_E8M0_BYTE}
+
+_lib = None
+
+
+class Fp8Error(RuntimeError):
+    """A negative status from libfp8blk."""
+
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+
+
+def lib():
+    """The loaded libfp8blk.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m fp8_block_scaled_02_amd.build` (there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.fp8b_abi_version.restype = ci
+        L.fp8b_abi_version.argtypes = []
+        L.fp8b_status_string.restype = ctypes.c_char_p
+        L.fp8b_status_string.argtypes = [ci]
+        L.fp8_act_quant.restype = ci
+        L.fp8_act_quant.argtypes = [vp, i64, i64, i64, ci, ci, vp, i64, vp, vp]
+        L.fp8_weight_quant.restype = ci
+        L.fp8_weight_quant.argtypes = [vp, i64, i64, i64, ci, vp, i64, vp, vp]
+        L.fp8_block_gemm.restype = ci
+        L.fp8_block_gemm.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, i64, vp, i64, ci, vp]
+        L.mxfp8_gemm.restype = ci
+        L.mxfp8_gemm.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, i64, vp, i64, vp]
+        L.fp8_grouped_gemm.restype = ci
+        L.fp8_grouped_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp, i64, i64, vp, ci, vp]
+        L.fp8_cast_f32.restype = ci
+        L.fp8_cast_f32.argtypes = [vp, i64, ci, vp, vp]
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return int(lib().fp8b_abi_version())
+
+
+def status_string(status: int) -> str:
+    return lib().fp8b_status_string(int(status)).decode()
+
+
+def _check(fn, rc):
+    if rc != FP8B_OK:
+        raise Fp8Error(fn, rc)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _fmt(scale_fmt):
+    return _SCALE_FMT[scale_fmt] if isinstance(scale_fmt, str) else int(scale_fmt)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def fp8_act_quant(x: torch.Tensor, block_k: int = 128, scale_fmt="fp32", q=None, scales=None):
+    """Dynamic per-token, per-block activation quantisation.
+
+    x: bf16 [M, K] on a GPU (row stride x.stride(0)).  Returns
+    (q uint8 [M, K], scales [M, K/block_k]) -- float32 scales, or uint8 E8M0
+    bytes for scale_fmt "e8m0"."""
+    _need(x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1, "x must be 2-D bf16, rows contiguous")
+    M, K = x.shape
+    f = _fmt(scale_fmt)
+    if q is None:
+        q = torch.empty(M, K, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        sdt = torch.uint8 if f == SCALE_E8M0_BYTE else torch.float32
+        scales = torch.empty(M, max(K // block_k, 0), dtype=sdt, device=x.device)
+    _need(q.stride(1) == 1 and scales.is_contiguous(), "q rows and scales must be contiguous")
+    rc = lib().fp8_act_quant(_p(x), M, K, x.stride(0) if M else K, block_k, f, _p(q),
+                             q.stride(0) if M else K, _p(scales), _stream(x))
+    _check("fp8_act_quant", rc)
+    return q, scales
+
+
+def fp8_weight_quant(w: torch.Tensor, scale_fmt="fp32", q=None, scales=None):
+    """128x128-block weight quantisation: w bf16 [N, K] -> (q uint8 [N, K],
+    float32 scales [N/128, K/128])."""
+    _need(w.dtype == torch.bfloat16 and w.dim() == 2 and w.stride(1) == 1, "w must be 2-D bf16, rows contiguous")
+    N, K = w.shape
+    if q is None:
+        q = torch.empty(N, K, dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(N // 128, K // 128, dtype=torch.float32, device=w.device)
+    rc = lib().fp8_weight_quant(_p(w), N, K, w.stride(0), _fmt(scale_fmt), _p(q), q.stride(0),
+                                _p(scales), _stream(w))
+    _check("fp8_weight_quant", rc)
+    return q, scales
+
+
+def fp8_block_gemm(a, a_scales, w, w_scales, out_dtype=torch.bfloat16, y=None):
+    """y[M, N] = block-scaled FP8 GEMM of codes a [M, K] and w [N, K] with
+    fp32 scales a_scales [M, K/128] and w_scales [N/128, K/128]."""
+    _need(a.dtype == torch.uint8 and w.dtype == torch.uint8, "codes must be uint8")
+    _need(a_scales.dtype == torch.float32 and w_scales.dtype == torch.float32, "scales must be float32")
+    M, K = a.shape
+    N = w.shape[0]
+    od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    if y is None:
+        y = torch.empty(M, N, dtype=out_dtype, device=a.device)
+    _need(y.stride(1) == 1, "y rows must be contiguous")
+    rc = lib().fp8_block_gemm(_p(a), a.stride(0) if M else K, _p(a_scales), _p(w), w.stride(0),
+                              _p(w_scales), M, N, K, _p(y), y.stride(0) if M else N, od, _stream(a))
+    _check("fp8_block_gemm", rc)
+    return y
+
+
+def mxfp8_gemm(a, a_e8m0, b, b_e8m0, y=None):
+    """y[M, N] (fp32) = MXFP8 GEMM of codes a [M, K], b [N, K] with E8M0
+    bytes a_e8m0 [M, K/32], b_e8m0 [N, K/32]."""
+    _need(a_e8m0.dtype == torch.uint8 and b_e8m0.dtype == torch.uint8, "E8M0 scales must be uint8")
+    M, K = a.shape
+    N = b.shape[0]
+    if y is None:
+        y = torch.empty(M, N, dtype=torch.float32, device=a.device)
+    rc = lib().mxfp8_gemm(_p(a), a.stride(0) if M else K, _p(a_e8m0), _p(b), b.stride(0), _p(b_e8m0),
+                          M, N, K, _p(y), y.stride(0) if M else N, _stream(a))
+    _check("mxfp8_gemm", rc)
+    return y
+
+
+def fp8_grouped_gemm(a, a_scales, row_index, expert_offsets, w, w_scales, out_dtype=torch.bfloat16, y=None):
+    """Grouped MoE GEMM: a [T, K] token codes, a_scales [T, K/128],
+    row_index int32 [R], expert_offsets int32 [E+1] (device), w [E, N, K],
+    w_scales [E, N/128, K/128] -> y [R, N] in routed order."""
+    _need(row_index.dtype == torch.int32 and expert_offsets.dtype == torch.int32, "routing must be int32")
+    _need(a.is_contiguous() and w.is_contiguous(), "a and w must be contiguous")
+    T, K = a.shape
+    E, N, _ = w.shape
+    R = row_index.shape[0]
+    od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    if y is None:
+        y = torch.empty(R, N, dtype=out_dtype, device=a.device)
+    rc = lib().fp8_grouped_gemm(_p(a), _p(a_scales), T, _p(row_index), _p(expert_offsets), R, E,
+                                _p(w), _p(w_scales), N, K, _p(y), od, _stream(a))
+    _check("fp8_grouped_gemm", rc)
+    return y
+
+
+def fp8_cast_f32(x: torch.Tensor, fmt=FMT_E4M3, q=None):
+    """FP8Cast with unit scale: clamp to +-Fmax, round to nearest even."""
+    _need(x.dtype == torch.float32 and x.is_contiguous(), "x must be contiguous float32")
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    rc = lib().fp8_cast_f32(_p(x), x.numel(), int(fmt), _p(q), _stream(x))
+    _check("fp8_cast_f32", rc)
+    return q
+
+
+def linear(x: torch.Tensor, w_q, w_scales, scale_fmt="fp32", out_dtype=torch.bfloat16):
+    """W8A8 linear layer: act_quant(x) then the block-scaled GEMM."""
+    a, sa = fp8_act_quant(x, 128, scale_fmt)
+    if sa.dtype != torch.float32:
+        raise ValueError("the block GEMM takes fp32 or ue8m0 (fp32-stored) scales")
+    return fp8_block_gemm(a, sa, w_q, w_scales, out_dtype)

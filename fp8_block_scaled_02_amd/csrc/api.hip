@@ -1,0 +1,112 @@
+// api.hip -- the C ABI of libfp8blk (declared in include/fp8blk.h): host-side
+// argument validation, then one launch on the caller's stream.  No
+// allocation, no synchronisation, no exceptions across the boundary.
+#include <stdint.h>
+#include <limits.h>
+
+#include "launch.hpp"
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every 32-bit tile index in range
+
+}  // namespace
+
+#define FP8B_EXPORT __attribute__((visibility("default")))
+
+extern "C" {
+
+FP8B_EXPORT int fp8b_abi_version(void) { return FP8B_ABI_VERSION; }
+
+FP8B_EXPORT const char* fp8b_status_string(int status) {
+  switch (status) {
+    case FP8B_OK: return "ok";
+    case FP8B_EINVAL: return "invalid argument (null pointer, size or multiple)";
+    case FP8B_EALIGN: return "misaligned pointer or leading dimension";
+    case FP8B_EUNSUPPORTED: return "unsupported format/enum value for this call";
+    case FP8B_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+FP8B_EXPORT int fp8_act_quant(const void* x, int64_t M, int64_t K, int64_t ld_x, int block_k, int scale_fmt, uint8_t* q,
+                  int64_t ld_q, void* scales, void* stream) {
+  if (block_k != 128 && block_k != 32) return FP8B_EUNSUPPORTED;
+  if (scale_fmt < FP8B_SCALE_FP32 || scale_fmt > FP8B_SCALE_E8M0_BYTE) return FP8B_EUNSUPPORTED;
+  if (scale_fmt == FP8B_SCALE_E8M0_BYTE && block_k != 32) return FP8B_EUNSUPPORTED;
+  if (!x || !q || !scales) return FP8B_EINVAL;
+  if (M < 0 || K <= 0 || M > kMaxDim || K > kMaxDim || K % block_k != 0) return FP8B_EINVAL;
+  if (ld_x < K || ld_q < K) return FP8B_EINVAL;
+  if (!aligned(x, 16) || ld_x % 8 != 0 || !aligned(q, 8) || ld_q % 8 != 0) return FP8B_EALIGN;
+  if (scale_fmt != FP8B_SCALE_E8M0_BYTE && !aligned(scales, 4)) return FP8B_EALIGN;
+  if (M * (K / 8) / 512 >= INT32_MAX) return FP8B_EINVAL;
+  if (M == 0) return FP8B_OK;
+  return fp8blk::launch_act_quant(x, M, K, ld_x, block_k, scale_fmt, q, ld_q, scales, as_stream(stream));
+}
+
+FP8B_EXPORT int fp8_weight_quant(const void* w, int64_t N, int64_t K, int64_t ld_w, int scale_fmt, uint8_t* q, int64_t ld_q,
+                     float* scales, void* stream) {
+  if (scale_fmt != FP8B_SCALE_FP32 && scale_fmt != FP8B_SCALE_UE8M0) return FP8B_EUNSUPPORTED;
+  if (!w || !q || !scales) return FP8B_EINVAL;
+  if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim || N % 128 != 0 || K % 128 != 0) return FP8B_EINVAL;
+  if (ld_w < K || ld_q < K) return FP8B_EINVAL;
+  if (!aligned(w, 16) || ld_w % 8 != 0 || !aligned(q, 8) || ld_q % 8 != 0 || !aligned(scales, 4))
+    return FP8B_EALIGN;
+  return fp8blk::launch_weight_quant(w, N, K, ld_w, scale_fmt, q, ld_q, scales, as_stream(stream));
+}
+
+FP8B_EXPORT int fp8_block_gemm(const uint8_t* a, int64_t ld_a, const float* a_scales, const uint8_t* w, int64_t ld_w,
+                   const float* w_scales, int64_t M, int64_t N, int64_t K, void* y, int64_t ld_y, int out_dtype,
+                   void* stream) {
+  if (out_dtype != FP8B_OUT_F32 && out_dtype != FP8B_OUT_BF16) return FP8B_EUNSUPPORTED;
+  if (!a || !a_scales || !w || !w_scales || !y) return FP8B_EINVAL;
+  if (M < 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8B_EINVAL;
+  if (N % 128 != 0 || K % 128 != 0 || ld_a < K || ld_w < K || ld_y < N) return FP8B_EINVAL;
+  if (!aligned(a, 16) || !aligned(w, 16) || ld_a % 16 != 0 || ld_w % 16 != 0) return FP8B_EALIGN;
+  if (!aligned(a_scales, 4) || !aligned(w_scales, 4) || !aligned(y, 16) || ld_y % 8 != 0) return FP8B_EALIGN;
+  if (((M + 127) / 128) * (N / 128) >= INT32_MAX) return FP8B_EINVAL;
+  if (M == 0) return FP8B_OK;
+  return fp8blk::launch_block_gemm(a, ld_a, a_scales, w, ld_w, w_scales, M, N, K, y, ld_y,
+                                   out_dtype == FP8B_OUT_BF16, as_stream(stream));
+}
+
+FP8B_EXPORT int mxfp8_gemm(const uint8_t* a, int64_t ld_a, const uint8_t* a_e8m0, const uint8_t* b, int64_t ld_b,
+               const uint8_t* b_e8m0, int64_t M, int64_t N, int64_t K, float* y, int64_t ld_y, void* stream) {
+  if (!a || !a_e8m0 || !b || !b_e8m0 || !y) return FP8B_EINVAL;
+  if (M < 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8B_EINVAL;
+  if (N % 128 != 0 || K % 128 != 0 || ld_a < K || ld_b < K || ld_y < N) return FP8B_EINVAL;
+  if (!aligned(a, 16) || !aligned(b, 16) || ld_a % 16 != 0 || ld_b % 16 != 0) return FP8B_EALIGN;
+  if (!aligned(a_e8m0, 4) || !aligned(b_e8m0, 4) || !aligned(y, 16) || ld_y % 4 != 0) return FP8B_EALIGN;
+  if (((M + 127) / 128) * (N / 128) >= INT32_MAX) return FP8B_EINVAL;
+  if (M == 0) return FP8B_OK;
+  return fp8blk::launch_mx_gemm(a, ld_a, a_e8m0, b, ld_b, b_e8m0, M, N, K, y, ld_y, as_stream(stream));
+}
+
+FP8B_EXPORT int fp8_grouped_gemm(const uint8_t* a, const float* a_scales, int64_t T, const int32_t* row_index,
+                     const int32_t* expert_offsets, int64_t R, int64_t E, const uint8_t* w, const float* w_scales,
+                     int64_t N, int64_t K, void* y, int out_dtype, void* stream) {
+  if (out_dtype != FP8B_OUT_F32 && out_dtype != FP8B_OUT_BF16) return FP8B_EUNSUPPORTED;
+  if (!a || !a_scales || !row_index || !expert_offsets || !w || !w_scales || !y) return FP8B_EINVAL;
+  if (T < 1 || R < 0 || E < 1 || E > 1024 || N <= 0 || K <= 0) return FP8B_EINVAL;
+  if (T > kMaxDim || R > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8B_EINVAL;
+  if (N % 128 != 0 || K % 128 != 0) return FP8B_EINVAL;
+  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(y, 16)) return FP8B_EALIGN;
+  if (!aligned(a_scales, 4) || !aligned(w_scales, 4) || !aligned(row_index, 4) || !aligned(expert_offsets, 4))
+    return FP8B_EALIGN;
+  if (R == 0) return FP8B_OK;
+  return fp8blk::launch_grouped_gemm(a, a_scales, T, row_index, expert_offsets, R, E, w, w_scales, N, K, y,
+                                     out_dtype == FP8B_OUT_BF16, as_stream(stream));
+}
+
+FP8B_EXPORT int fp8_cast_f32(const float* x, int64_t n, int fmt, uint8_t* q, void* stream) {
+  if (fmt != FP8B_FMT_E4M3 && fmt != FP8B_FMT_E5M2) return FP8B_EUNSUPPORTED;
+  if (!x || !q || n < 0) return FP8B_EINVAL;
+  if (!aligned(x, 4)) return FP8B_EALIGN;
+  if (n / 1024 >= INT32_MAX) return FP8B_EINVAL;
+  if (n == 0) return FP8B_OK;
+  return fp8blk::launch_cast(x, n, fmt, q, as_stream(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of libfp8blk.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8blk {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// E8M0 byte meaning 2^0 for the scaled MFMA (exponent bias 127).
+constexpr int kUnitScale = 127;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// max over the 16 lanes of a DPP row (quad swaps, then half-row and row
+// mirrors); every lane of the row ends with the row maximum.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
+// max over each aligned quad of lanes.
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  return v;
+}
+
+// Exponent e of the power-of-two scale: smallest integer with
+// amax <= 448 * 2^e, clamped to [-127, 127]; 0 for amax == 0.
+// With amax = sig * 2^E (sig in [1, 2)), amax / 448 = (sig / 1.75) * 2^(E-8),
+// so e = E - 8 + (sig > 1.75).  Subnormal amax lies far below 448 * 2^-127.
+__device__ __forceinline__ int pow2_scale_exp(float amax) {
+  uint32_t u = __float_as_uint(amax) & 0x7fffffffu;
+  if (u == 0) return 0;
+  int ef = (int)(u >> 23);
+  if (ef == 0) return -127;
+  int e = ef - 127 - 8 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// 2^e as fp32 for e in [-127, 127] (2^-127 is a subnormal).
+__device__ __forceinline__ float exp2i(int e) {
+  return e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// Pack four fp32 values (already clamped to +-448) into four E4M3 bytes,
+// round to nearest even.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+
+__device__ __forceinline__ uint32_t pack4_e5m2(float a, float b, float c, float d) {
+  int r = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+
+__device__ __forceinline__ float clamp448(float v) {
+  return fminf(fmaxf(v, -448.0f), 448.0f);
+}
+
+}  // namespace fp8blk

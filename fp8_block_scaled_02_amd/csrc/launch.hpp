@@ -1,0 +1,30 @@
+// launch.hpp -- host-side launch plumbing shared by the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fp8blk.h"
+
+namespace fp8blk {
+
+inline int check_launch() {
+  return hipGetLastError() == hipSuccess ? FP8B_OK : FP8B_ELAUNCH;
+}
+
+int launch_act_quant(const void* x, int64_t M, int64_t K, int64_t ldx, int block, int fmt,
+                     uint8_t* q, int64_t ldq, void* scales, hipStream_t s);
+int launch_weight_quant(const void* w, int64_t N, int64_t K, int64_t ldw, int fmt, uint8_t* q,
+                        int64_t ldq, float* scales, hipStream_t s);
+int launch_cast(const float* x, int64_t n, int fmt, uint8_t* q, hipStream_t s);
+int launch_block_gemm(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w,
+                      int64_t ldw, const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                      int64_t ldy, int out_bf16, hipStream_t s);
+int launch_mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* ea, const uint8_t* b,
+                   int64_t ldb, const uint8_t* eb, int64_t M, int64_t N, int64_t K, float* y,
+                   int64_t ldy, hipStream_t s);
+int launch_grouped_gemm(const uint8_t* a, const float* sa, int64_t T, const int32_t* row_index,
+                        const int32_t* offs, int64_t R, int64_t E, const uint8_t* w,
+                        const float* sw, int64_t N, int64_t K, void* y, int out_bf16,
+                        hipStream_t s);
+
+}  // namespace fp8blk

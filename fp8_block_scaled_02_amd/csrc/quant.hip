@@ -1,0 +1,212 @@
+// quant.hip -- quantisation kernels for gfx950.
+//
+// act_quant: per token, per block of 128 (or 32) channels, amax -> scale ->
+// E4M3 codes (DeepSeek-V3 guide, runtime-dispatch snippet; quantizer of
+// "FP8 engineering 2026" section 2; Dynamic Scaling of the "FP8 推理"
+// notes: scale = amax / 448, fp8 = x / scale).
+//
+// The work is HBM-bound (2 bytes in, 1 byte + a scale out per element), so
+// the kernel is built for streaming: every lane owns 8 consecutive bf16
+// (one 16-byte load), the lanes of one quantisation block are adjacent in a
+// wavefront, the block maximum is reduced with DPP inside the wave (no LDS,
+// no barrier), and each lane writes its 8 codes with one 8-byte store.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace fp8blk {
+
+// FMT: 0 fp32 scales, 1 power-of-two scales stored as fp32, 2 E8M0 bytes.
+template <int BLOCK, int FMT, int UNROLL>
+__global__ __launch_bounds__(256) void act_quant_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+    uint8_t* __restrict__ q, int64_t ldq, void* __restrict__ scales) {
+  constexpr int LPB = BLOCK / 8;  // lanes per quantisation block
+  const int64_t cpr = K / 8;      // 16-byte chunks per row
+  const int64_t total = M * cpr;
+  const int64_t nblk = K / BLOCK;
+  const int64_t base = ((int64_t)blockIdx.x * 256 * UNROLL) + threadIdx.x;
+
+  uint4 raw[UNROLL];
+  int64_t row[UNROLL], col[UNROLL];
+  bool ok[UNROLL];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int64_t c = base + (int64_t)u * 256;
+    ok[u] = c < total;
+    row[u] = ok[u] ? c / cpr : 0;
+    col[u] = ok[u] ? (c - row[u] * cpr) * 8 : 0;
+    raw[u] = ok[u] ? *reinterpret_cast<const uint4*>(x + row[u] * ldx + col[u])
+                   : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    float f[8];
+    const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+      f[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = (LPB == 16) ? row16_max(amax) : quad_max(amax);
+
+    float qv[8];
+    int e = 0;
+    if (FMT == 0) {
+      const float d = (amax == 0.0f) ? 1.0f : amax / 448.0f;  // IEEE division
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[i] = clamp448(f[i] / d);
+      if (ok[u] && (col[u] % BLOCK) == 0)
+        reinterpret_cast<float*>(scales)[row[u] * nblk + col[u] / BLOCK] = d;
+    } else {
+      e = pow2_scale_exp(amax);
+      // x / 2^e == x * 2^-e exactly (both are the correctly rounded quotient)
+      const float rinv = exp2i(-e);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[i] = clamp448(f[i] * rinv);
+      if (ok[u] && (col[u] % BLOCK) == 0) {
+        if (FMT == 1)
+          reinterpret_cast<float*>(scales)[row[u] * nblk + col[u] / BLOCK] = exp2i(e);
+        else
+          reinterpret_cast<uint8_t*>(scales)[row[u] * nblk + col[u] / BLOCK] = (uint8_t)(127 + e);
+      }
+    }
+    if (ok[u]) {
+      uint2 out;
+      out.x = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
+      out.y = pack4_e4m3(qv[4], qv[5], qv[6], qv[7]);
+      *reinterpret_cast<uint2*>(q + row[u] * ldq + col[u]) = out;
+    }
+  }
+}
+
+// Weight quantisation: one workgroup per 128x128 tile.  256 threads, each
+// owns 8 chunks of 8 bf16; amax is reduced in-wave with DPP, across waves
+// through LDS.
+template <int FMT>
+__global__ __launch_bounds__(256) void weight_quant_kernel(
+    const uint16_t* __restrict__ w, int64_t N, int64_t K, int64_t ldw,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales) {
+  __shared__ float red[4];
+  const int64_t kt = K / 128;
+  const int64_t ti = blockIdx.x / kt, tj = blockIdx.x % kt;
+  const int tid = threadIdx.x;
+  uint4 raw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c >> 4, ch = c & 15;
+    raw[i] = *reinterpret_cast<const uint4*>(w + (ti * 128 + r) * ldw + tj * 128 + ch * 8);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t v[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[j] & 0xffffu)));
+      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[j] >> 16)));
+    }
+  }
+  amax = row16_max(amax);
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+  float d, rinv = 1.0f;
+  if (FMT == 0) {
+    d = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+  } else {
+    const int e = pow2_scale_exp(amax);
+    d = exp2i(e);
+    rinv = exp2i(-e);
+  }
+  if (tid == 0) scales[ti * kt + tj] = d;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c >> 4, ch = c & 15;
+    const uint32_t v[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[2 * j] = bf16_bits_to_f32(v[j] & 0xffffu);
+      f[2 * j + 1] = bf16_bits_to_f32(v[j] >> 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = clamp448(FMT == 0 ? f[j] / d : f[j] * rinv);
+    uint2 out;
+    out.x = pack4_e4m3(f[0], f[1], f[2], f[3]);
+    out.y = pack4_e4m3(f[4], f[5], f[6], f[7]);
+    *reinterpret_cast<uint2*>(q + (ti * 128 + r) * ldq + tj * 128 + ch * 8) = out;
+  }
+}
+
+// FP8Cast with s = 1: clamp to +-Fmax, round to nearest even.  4 values per
+// thread.
+template <int FMT>
+__global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ x, int64_t n,
+                                                   uint8_t* __restrict__ q) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float t = (i + j < n) ? x[i + j] : 0.0f;
+    v[j] = FMT == 0 ? clamp448(t) : fminf(fmaxf(t, -57344.0f), 57344.0f);
+  }
+  const uint32_t p = FMT == 0 ? pack4_e4m3(v[0], v[1], v[2], v[3]) : pack4_e5m2(v[0], v[1], v[2], v[3]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (i + j < n) q[i + j] = (uint8_t)(p >> (8 * j));
+}
+
+// ---- host launchers --------------------------------------------------------
+constexpr int kActUnroll = 2;
+
+int launch_act_quant(const void* x, int64_t M, int64_t K, int64_t ldx, int block, int fmt,
+                     uint8_t* q, int64_t ldq, void* scales, hipStream_t s) {
+  const int64_t total = M * (K / 8);
+  const int64_t per_wg = 256 * kActUnroll;
+  const dim3 grid((unsigned)((total + per_wg - 1) / per_wg));
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+#define FP8B_AQ(B, F) \
+  hipLaunchKernelGGL((act_quant_kernel<B, F, kActUnroll>), grid, dim3(256), 0, s, xp, M, K, ldx, q, ldq, scales)
+  if (block == 128) {
+    if (fmt == 0) FP8B_AQ(128, 0);
+    else if (fmt == 1) FP8B_AQ(128, 1);
+    else FP8B_AQ(128, 2);
+  } else {
+    if (fmt == 0) FP8B_AQ(32, 0);
+    else if (fmt == 1) FP8B_AQ(32, 1);
+    else FP8B_AQ(32, 2);
+  }
+#undef FP8B_AQ
+  return check_launch();
+}
+
+int launch_weight_quant(const void* w, int64_t N, int64_t K, int64_t ldw, int fmt, uint8_t* q,
+                        int64_t ldq, float* scales, hipStream_t s) {
+  const dim3 grid((unsigned)((N / 128) * (K / 128)));
+  const uint16_t* wp = static_cast<const uint16_t*>(w);
+  if (fmt == 0)
+    hipLaunchKernelGGL(weight_quant_kernel<0>, grid, dim3(256), 0, s, wp, N, K, ldw, q, ldq, scales);
+  else
+    hipLaunchKernelGGL(weight_quant_kernel<1>, grid, dim3(256), 0, s, wp, N, K, ldw, q, ldq, scales);
+  return check_launch();
+}
+
+int launch_cast(const float* x, int64_t n, int fmt, uint8_t* q, hipStream_t s) {
+  const dim3 grid((unsigned)((n + 1023) / 1024));
+  if (fmt == 0)
+    hipLaunchKernelGGL(cast_kernel<0>, grid, dim3(256), 0, s, x, n, q);
+  else
+    hipLaunchKernelGGL(cast_kernel<1>, grid, dim3(256), 0, s, x, n, q);
+  return check_launch();
+}
+
+}  // namespace fp8blk

@@ -1,0 +1,206 @@
+/*
+ * fp8blk.h -- C ABI of the MI355X (gfx950) W8A8 block-scaled FP8 linear
+ * layer library (libfp8blk.so).
+ *
+ * What it computes (sources named by page title and section):
+ *  - "FP8 推理提速 83.6%: DeepSeek-V3 在 AMD MI250 上的完整落地指南",
+ *    runtime-dispatch snippet: a linear layer in fp8 mode runs
+ *    act_quant(x, block_size, scale_fmt) -> (x_fp8, scale) and then
+ *    fp8_gemm(x, scale, weight, weight.scale); its configuration table fixes
+ *    E4M3 weights with one scale per 128x128 block, scale_fmt ue8m0, 256
+ *    routed experts and 8 active experts per token.
+ *  - "LLM 推理的 FP8 混合精度工程 2026", section 2: the quantizer
+ *    Q(x) = clamp(round(x*s), -Fmax, Fmax) * s^-1 with Fmax = 448 (E4M3),
+ *    57344 (E5M2); section 3: FP32 accumulation and blockwise scales.
+ *  - "FP8 推理" study notes, Dynamic Scaling: scale = max|x| / 448 and
+ *    fp8 value = x / scale.
+ *  - "量化: FP8 与混合精度推理", section "FP8 也需要 scale":
+ *    x_fp8 = FP8Cast(x / s), x_hat = s * x_fp8.
+ *  - ROCm 7.0 FP8/MXFP8 article, sections 1.1-1.2: MXFP8 = 32-element
+ *    blocks sharing one 8-bit exponent (E8M0).
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or keeps them after the call returns.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default
+ *    stream.  Work is enqueued asynchronously; FP8B_OK means the launch was
+ *    accepted, not that the kernel finished.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    negative status means nothing was launched (except FP8B_ELAUNCH).
+ *  - Matrices are row-major with a leading dimension `ld_*` in elements.
+ *    "Codes" are E4M3 (OCP, no Inf, largest finite 448) bytes.
+ *  - Scale d is the dequantisation multiplier: x ~= d * value(code).
+ *    Codes are computed from the fp32 quotient x / d, clamped to +-448 and
+ *    rounded to nearest, ties to even.  A negative value that rounds to
+ *    zero gives code 0x80.
+ *  - Non-finite inputs give unspecified codes/outputs but never fault.
+ *  - Thread-safe; no global mutable state.
+ */
+#ifndef FP8BLK_H
+#define FP8BLK_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8B_ABI_VERSION 1
+
+typedef enum {
+  FP8B_OK = 0,
+  FP8B_EINVAL = -1,       /* NULL pointer, bad size, size not a multiple  */
+  FP8B_EALIGN = -2,       /* pointer or leading dimension misaligned      */
+  FP8B_EUNSUPPORTED = -3, /* enum value not valid for this call          */
+  FP8B_ELAUNCH = -4       /* the HIP launch failed (hipGetLastError)     */
+} fp8b_status;
+
+typedef enum {
+  FP8B_SCALE_FP32 = 0,      /* fp32 d = fp32(amax / 448); d = 1 if amax=0 */
+  FP8B_SCALE_UE8M0 = 1,     /* fp32 storage of d = 2^e, e the smallest
+                               integer with amax <= 448 * 2^e, clamped to
+                               [-127, 127]; e = 0 if amax = 0            */
+  FP8B_SCALE_E8M0_BYTE = 2  /* the same e stored as one byte 127 + e      */
+} fp8b_scale_fmt;
+
+typedef enum { FP8B_OUT_F32 = 0, FP8B_OUT_BF16 = 1 } fp8b_out_dtype;
+
+typedef enum { FP8B_FMT_E4M3 = 0, FP8B_FMT_E5M2 = 1 } fp8b_elem_fmt;
+
+/* Version of this ABI (FP8B_ABI_VERSION). */
+int fp8b_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char *fp8b_status_string(int status);
+
+/*
+ * fp8_act_quant -- dynamic activation quantisation (act_quant of the
+ * DeepSeek-V3 guide's dispatch snippet; Dynamic Scaling of the "FP8 推理"
+ * notes; quantizer of "FP8 engineering 2026" section 2).
+ *
+ *   For every row m and block j of `block_k` consecutive columns:
+ *     amax = max |x[m][j*block_k ...]|, d from `scale_fmt`,
+ *     q[m][k] = E4M3(clamp(fp32(x[m][k] / d), -448, 448)).
+ *
+ *   x       bf16 [M][ld_x], 16-byte aligned, ld_x % 8 == 0, ld_x >= K.
+ *   M       rows (tokens), >= 0 (0 is a no-op).
+ *   K       columns, > 0, K % block_k == 0.
+ *   block_k 128 (per token per 128 channels) or 32 (MX blocks).
+ *   scale_fmt FP8B_SCALE_FP32 | FP8B_SCALE_UE8M0 (fp32 scales) or
+ *           FP8B_SCALE_E8M0_BYTE (one byte per block; block_k must be 32).
+ *   q       uint8 codes [M][ld_q], 8-byte aligned, ld_q % 8 == 0, >= K.
+ *   scales  [M][K/block_k], contiguous: float (4-byte aligned) or uint8.
+ */
+int fp8_act_quant(const void *x, int64_t M, int64_t K, int64_t ld_x,
+                  int block_k, int scale_fmt, uint8_t *q, int64_t ld_q,
+                  void *scales, void *stream);
+
+/*
+ * fp8_weight_quant -- offline weight quantisation with one scale per
+ * 128x128 block (the "FP8 weights carry 128x128 block scales
+ * (weight_scale_inv)" statement of the DeepSeek-V3 guide, scale_fmt ue8m0
+ * in its configuration table).  Same rule as fp8_act_quant with amax taken
+ * over each 128x128 tile.
+ *
+ *   w       bf16 [N][ld_w], 16-byte aligned, ld_w % 8 == 0, ld_w >= K.
+ *   N, K    > 0, multiples of 128.
+ *   scale_fmt FP8B_SCALE_FP32 or FP8B_SCALE_UE8M0.
+ *   q       uint8 [N][ld_q], 8-byte aligned, ld_q % 8 == 0, ld_q >= K.
+ *   scales  float [N/128][K/128], contiguous.
+ */
+int fp8_weight_quant(const void *w, int64_t N, int64_t K, int64_t ld_w,
+                     int scale_fmt, uint8_t *q, int64_t ld_q, float *scales,
+                     void *stream);
+
+/*
+ * fp8_block_gemm -- block-scaled FP8 GEMM (fp8_gemm(x, scale, weight,
+ * weight.scale) of the DeepSeek-V3 guide; blockwise per-block-scale GEMM
+ * with FP32 accumulation of "FP8 engineering 2026" section 3).
+ *
+ *   y[m][n] = sum_kb a_scales[m][kb] * w_scales[n/128][kb] *
+ *             sum_{k in block kb} value(a[m][k]) * value(w[n][k])
+ *   with fp32 accumulation and a per-128-K-block rescale; y is written as
+ *   fp32 or bf16 (round to nearest even).
+ *
+ *   a         codes [M][ld_a], 16-byte aligned, ld_a % 16 == 0, >= K.
+ *   a_scales  float [M][K/128], contiguous (fp8_act_quant with block 128).
+ *   w         codes [N][ld_w], 16-byte aligned, ld_w % 16 == 0, >= K.
+ *   w_scales  float [N/128][K/128], contiguous.
+ *   M >= 0 (0 is a no-op); N, K > 0 and multiples of 128.
+ *   y         [M][ld_y] fp32 or bf16, 16-byte aligned, ld_y >= N,
+ *             ld_y % 8 == 0.
+ *   out_dtype FP8B_OUT_F32 or FP8B_OUT_BF16.
+ */
+int fp8_block_gemm(const uint8_t *a, int64_t ld_a, const float *a_scales,
+                   const uint8_t *w, int64_t ld_w, const float *w_scales,
+                   int64_t M, int64_t N, int64_t K, void *y, int64_t ld_y,
+                   int out_dtype, void *stream);
+
+/*
+ * mxfp8_gemm -- MXFP8 GEMM (ROCm 7.0 FP8 article, sections 1.1-1.2: blocks
+ * of 32 elements along K share one E8M0 exponent).
+ *
+ *   y[m][n] = sum_kb 2^(a_e8m0[m][kb] - 127) * 2^(b_e8m0[n][kb] - 127) *
+ *             sum_{k in 32-block kb} value(a[m][k]) * value(b[n][k])
+ *   accumulated in fp32, written as fp32.
+ *
+ *   a       codes [M][ld_a]; b codes [N][ld_b]; both 16-byte aligned,
+ *           ld % 16 == 0, ld >= K.
+ *   a_e8m0  uint8 [M][K/32]; b_e8m0 uint8 [N][K/32]; contiguous, 4-byte
+ *           aligned (fp8_act_quant with block 32, FP8B_SCALE_E8M0_BYTE).
+ *   M >= 0; N, K > 0 and multiples of 128.
+ *   y       float [M][ld_y], 16-byte aligned, ld_y % 4 == 0, ld_y >= N.
+ *   Scale byte 0xFF (NaN) gives unspecified outputs.
+ */
+int mxfp8_gemm(const uint8_t *a, int64_t ld_a, const uint8_t *a_e8m0,
+               const uint8_t *b, int64_t ld_b, const uint8_t *b_e8m0,
+               int64_t M, int64_t N, int64_t K, float *y, int64_t ld_y,
+               void *stream);
+
+/*
+ * fp8_grouped_gemm -- grouped block-scaled GEMM for mixture-of-experts
+ * layers (the DeepSeek-V3 guide's 256 routed / 8 active experts; the
+ * block-scale fused MoE operator of the ROCm 7.0 article, section 2).
+ *
+ *   Output row r (0 <= r < R) belongs to the expert e with
+ *   expert_offsets[e] <= r < expert_offsets[e+1] and reads token
+ *   t = row_index[r]:
+ *     y[r][n] = sum_kb a_scales[t][kb] * w_scales[e][n/128][kb] *
+ *               sum_{k in kb} value(a[t][k]) * value(w[e][n][k])
+ *   (the gather happens inside the kernel; rows are written in routed
+ *   order).  The per-expert tile map is derived on the device from
+ *   expert_offsets: no host synchronisation and no workspace.
+ *
+ *   a               token codes [T][K] (contiguous, 16-byte aligned).
+ *   a_scales        float [T][K/128].
+ *   row_index       int32 [R] (device) token of each routed row.
+ *   expert_offsets  int32 [E+1] (device), non-decreasing, [0] = 0,
+ *                   [E] = R.  Entries outside that contract, or token ids
+ *                   outside [0, T), give unspecified rows but never fault.
+ *   T >= 1, R >= 0 (0 is a no-op), 1 <= E <= 1024.
+ *   w               codes [E][N][K] (contiguous, 16-byte aligned).
+ *   w_scales        float [E][N/128][K/128].
+ *   N, K            > 0, multiples of 128.
+ *   y               [R][N] fp32 or bf16, 16-byte aligned.
+ *   out_dtype       FP8B_OUT_F32 or FP8B_OUT_BF16.
+ */
+int fp8_grouped_gemm(const uint8_t *a, const float *a_scales, int64_t T,
+                     const int32_t *row_index, const int32_t *expert_offsets,
+                     int64_t R, int64_t E, const uint8_t *w,
+                     const float *w_scales, int64_t N, int64_t K, void *y,
+                     int out_dtype, void *stream);
+
+/*
+ * fp8_cast_f32 -- FP8Cast of "量化: FP8 与混合精度推理" (x_fp8 =
+ * FP8Cast(x / s)) with s = 1: clamp each fp32 value to +-Fmax (448 for
+ * E4M3, 57344 for E5M2) and round to nearest, ties to even.
+ *
+ *   x    float [n] (4-byte aligned); n >= 0.
+ *   fmt  FP8B_FMT_E4M3 or FP8B_FMT_E5M2.
+ *   q    uint8 [n].
+ */
+int fp8_cast_f32(const float *x, int64_t n, int fmt, uint8_t *q, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

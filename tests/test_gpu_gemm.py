@@ -1,0 +1,203 @@
+"""GPU parity of the GEMM kernels (block-scaled, MXFP8, grouped MoE) against
+the CPU oracle.
+
+Each side quantises the same seeded bf16 inputs itself (the quantisers are
+proven bit-identical in test_gpu_quant.py); the oracle then computes y with
+exact block sums and an fp64 combination, and the GPU output must meet the
+tolerance in tests/parity.py.  Small cases are compared element by element;
+full-size cases on sampled rows (each sampled row covers every column, so
+every N tile and both ends of the M range are checked).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def F():
+    import fp8_block_scaled_02_amd as F
+    assert torch.cuda.is_available()
+    return F
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _linear_case(F, orc, x, w, fmt, out_dtype, rows=None):
+    """Run act_quant + weight quant + block GEMM on the GPU; the oracle
+    recomputes everything from the bf16 inputs for the given rows."""
+    fi = {"fp32": 0, "ue8m0": 1}[fmt]
+    a, sa = F.fp8_act_quant(x.to(DEV), 128, fmt)
+    wq, ws = F.fp8_weight_quant(w.to(DEV), fmt)
+    y = F.fp8_block_gemm(a, sa, wq, ws, out_dtype)
+    torch.cuda.synchronize()
+    xs = x if rows is None else x[torch.as_tensor(rows, device=x.device)]
+    oa, osa = orc.act_quant(W.bits(xs), 128, fi)
+    ow, osw = orc.weight_quant(W.bits(w), fi)
+    yr, bnd = orc.block_gemm(oa, osa, ow, osw)
+    yg = _np(y) if rows is None else _np(y[torch.as_tensor(rows, device=y.device)])
+    return yg, yr, bnd
+
+
+def test_block_gemm_tiny_fp32(F, orc):
+    c = W.tiny_linear()
+    yg, yr, bnd = _linear_case(F, orc, c.x, c.w, "fp32", torch.float32)
+    worst = assert_parity(yg, yr, bnd, False, "tiny")
+    print(f"tiny worst err/allowed {worst:.3g}")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 384, 640), (1, 128, 128), (129, 256, 256), (64, 512, 1280)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_block_gemm_ragged(F, orc, M, N, K, out):
+    c = W.prefill_linear(M=M, K=K, N=N, seed=M + N + K)
+    yg, yr, bnd = _linear_case(F, orc, c.x, c.w, "fp32", out)
+    assert_parity(yg, yr, bnd, out == torch.bfloat16, f"{M}x{N}x{K}")
+
+
+def test_block_gemm_ue8m0_small(F, orc):
+    c = W.decode_linear(K=1024, N=512)
+    yg, yr, bnd = _linear_case(F, orc, c.x, c.w, "ue8m0", torch.bfloat16)
+    assert_parity(yg, yr, bnd, True, "ue8m0 128x512x1024")
+
+
+def test_block_gemm_decode_full(F, orc):
+    c = W.decode_linear(device=DEV)
+    a, sa = F.fp8_act_quant(c.x, 128, "ue8m0")
+    wq, ws = F.fp8_weight_quant(c.w, "ue8m0")
+    ow, osw = orc.weight_quant(W.bits(c.w), 1)
+    for M in (1, 8, 32, 128):
+        y = F.fp8_block_gemm(a[:M], sa[:M], wq, ws, torch.bfloat16)
+        torch.cuda.synchronize()
+        rows = sorted({0, M - 1, M // 2})
+        oa, osa = orc.act_quant(W.bits(c.x[rows]), 128, 1)
+        yr, bnd = orc.block_gemm(oa, osa, ow, osw)
+        assert_parity(_np(y[rows]), yr, bnd, True, f"decode M={M}")
+
+
+def test_block_gemm_prefill_full_sampled(F, orc):
+    c = W.prefill_linear(device=DEV)
+    rows = [0, 1, 127, 128, 1000, 2047, 2048, 3071, 4094, 4095]
+    yg, yr, bnd = _linear_case(F, orc, c.x, c.w, "fp32", torch.bfloat16, rows=rows)
+    worst = assert_parity(yg, yr, bnd, True, "prefill 4096x18432x7168")
+    print(f"prefill worst err/allowed {worst:.3g}")
+
+
+def test_block_gemm_deterministic(F):
+    c = W.prefill_linear(device=DEV, M=256, N=1024, K=2048)
+    a, sa = F.fp8_act_quant(c.x, 128, "fp32")
+    wq, ws = F.fp8_weight_quant(c.w, "fp32")
+    y1 = F.fp8_block_gemm(a, sa, wq, ws, torch.bfloat16)
+    y2 = F.fp8_block_gemm(a, sa, wq, ws, torch.bfloat16)
+    assert torch.equal(y1, y2)
+
+
+# ---- MXFP8 -------------------------------------------------------------------
+def _mx_case(F, orc, a_bf, b_bf, rows=None):
+    qa, ea = F.fp8_act_quant(a_bf.to(DEV), 32, "e8m0")
+    qb, eb = F.fp8_act_quant(b_bf.to(DEV), 32, "e8m0")
+    y = F.mxfp8_gemm(qa, ea, qb, eb)
+    torch.cuda.synchronize()
+    asel = a_bf if rows is None else a_bf[torch.as_tensor(rows, device=a_bf.device)]
+    oa, oea = orc.act_quant(W.bits(asel), 32, 2)
+    ob, oeb = orc.act_quant(W.bits(b_bf), 32, 2)
+    yr, bnd = orc.mx_gemm(oa, oea, ob, oeb)
+    yg = _np(y) if rows is None else _np(y[torch.as_tensor(rows, device=y.device)])
+    return yg, yr, bnd
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 256, 512), (16, 128, 128), (130, 384, 640)])
+def test_mx_gemm_small(F, orc, M, N, K):
+    a, b = W.mx_case(M=M, N=N, K=K, seed=M + K)
+    yg, yr, bnd = _mx_case(F, orc, a, b)
+    worst = assert_parity(yg, yr, bnd, False, f"mx {M}x{N}x{K}")
+    print(f"mx {M}x{N}x{K} worst {worst:.3g}")
+
+
+def test_mx_gemm_unit_scales_equal_plain_products(F, orc):
+    """All E8M0 bytes 127: the MX GEMM is a plain FP8 GEMM (exact integer
+    sums here: codes of small integers)."""
+    ints = np.arange(-6, 7)
+    code = {v: int(orc.e4m3_encode(np.array([v], np.float32))[0]) for v in ints}
+    rng = np.random.default_rng(4)
+    ia = rng.choice(ints, size=(64, 256))
+    ib = rng.choice(ints, size=(128, 256))
+    qa = torch.from_numpy(np.vectorize(code.get)(ia).astype(np.uint8)).to(DEV)
+    qb = torch.from_numpy(np.vectorize(code.get)(ib).astype(np.uint8)).to(DEV)
+    ea = torch.full((64, 8), 127, dtype=torch.uint8, device=DEV)
+    eb = torch.full((128, 8), 127, dtype=torch.uint8, device=DEV)
+    y = F.mxfp8_gemm(qa, ea, qb, eb)
+    np.testing.assert_array_equal(_np(y), (ia @ ib.T).astype(np.float64))
+
+
+def test_mx_gemm_full_sampled(F, orc):
+    a, b = W.mx_case(device=DEV)
+    rows = [0, 127, 128, 4095, 8190, 8191]
+    yg, yr, bnd = _mx_case(F, orc, a, b, rows=rows)
+    worst = assert_parity(yg, yr, bnd, False, "mx 8192^3")
+    print(f"mx 8192^3 worst {worst:.3g}")
+
+
+# ---- grouped MoE ---------------------------------------------------------------
+def _moe_run(F, orc, case, rows=None):
+    x = case.x.to(DEV)
+    a, sa = F.fp8_act_quant(x, 128, "fp32")
+    E, N, K = case.w.shape
+    wq = torch.empty(E, N, K, dtype=torch.uint8, device=DEV)
+    ws = torch.empty(E, N // 128, K // 128, dtype=torch.float32, device=DEV)
+    for e in range(E):
+        F.fp8_weight_quant(case.w[e].to(DEV), "fp32", q=wq[e], scales=ws[e])
+    ri = case.row_index.to(DEV)
+    offs = case.offs.to(DEV)
+    y = F.fp8_grouped_gemm(a, sa, ri, offs, wq, ws, torch.bfloat16)
+    torch.cuda.synchronize()
+    R = case.row_index.shape[0]
+    rows = np.arange(R) if rows is None else np.asarray(rows)
+    offs_np = case.offs.numpy()
+    experts = sorted({int(np.searchsorted(offs_np, r, side="right") - 1) for r in rows})
+    toks = sorted({int(case.row_index[r]) for r in rows})
+    # the oracle quantises the tokens and experts it needs from the bf16 inputs
+    oa_full = np.zeros((case.x.shape[0], K), np.uint8)
+    osa_full = np.ones((case.x.shape[0], K // 128), np.float32)
+    oa, osa = orc.act_quant(W.bits(case.x[torch.as_tensor(toks, device=case.x.device)]), 128, 0)
+    oa_full[toks] = oa
+    osa_full[toks] = osa
+    wl, sl = [None] * E, [None] * E
+    for e in experts:
+        wl[e], sl[e] = orc.weight_quant(W.bits(case.w[e]), 0)
+    yr, bnd = orc.grouped_gemm(oa_full, osa_full, case.row_index.numpy(), offs_np, wl, sl, rows=rows)
+    return _np(y[torch.as_tensor(rows, device=y.device)]), yr, bnd
+
+
+def test_grouped_small_full(F, orc):
+    case = W.moe_case(T=64, E=8, topk=2, N=256, K=384)
+    yg, yr, bnd = _moe_run(F, orc, case)
+    assert_parity(yg, yr, bnd, True, "moe small")
+
+
+def test_grouped_skewed_with_empty_experts(F, orc):
+    case = W.moe_case(T=300, E=32, topk=3, N=256, K=256, s=2.0)
+    counts = (case.offs[1:] - case.offs[:-1]).numpy()
+    assert (counts == 0).any() and counts.max() > 128
+    yg, yr, bnd = _moe_run(F, orc, case)
+    assert_parity(yg, yr, bnd, True, "moe skewed")
+
+
+def test_grouped_full_sampled(F, orc):
+    case = W.moe_case(device=DEV)
+    offs = case.offs.numpy()
+    counts = offs[1:] - offs[:-1]
+    big = int(np.argmax(counts))
+    small = [e for e in range(len(counts)) if counts[e] == 1][:3]
+    rows = {0, int(offs[-1]) - 1, int(offs[big]), int(offs[big + 1]) - 1, int(offs[big]) + 130}
+    rows |= {int(offs[e]) for e in small}
+    rows = sorted(rows)
+    yg, yr, bnd = _moe_run(F, orc, case, rows=rows)
+    worst = assert_parity(yg, yr, bnd, True, "moe 256 experts")
+    print(f"moe full worst {worst:.3g}; rows {rows}")

@@ -1,0 +1,177 @@
+"""GPU parity of the quantisation kernels against the CPU oracle.
+
+Codes and scales must match bit for bit.  Inputs are the seeded synthetic
+workloads (small case, decode, prefill, MX operands) plus hand-made edge
+cases; the oracle quantises the same bf16 values on the CPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def F():
+    import fp8_block_scaled_02_amd as F
+    assert torch.cuda.is_available()
+    return F
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _run_act(F, orc, x, block, fmt):
+    fi = {"fp32": 0, "ue8m0": 1, "e8m0": 2}[fmt]
+    q, s = F.fp8_act_quant(x.to(DEV), block, fmt)
+    torch.cuda.synchronize()
+    q2, s2 = orc.act_quant(W.bits(x), block, fi)
+    return _np(q), _np(s), q2, s2
+
+
+def _assert_same(q, s, q2, s2, what):
+    bad = np.argwhere(q != q2)
+    assert len(bad) == 0, f"{what}: {len(bad)} code mismatches, first at {tuple(bad[0])}: gpu {q[tuple(bad[0])]:#x} oracle {q2[tuple(bad[0])]:#x}"
+    sv, sv2 = s.view(np.uint8), s2.view(np.uint8)
+    bad = np.argwhere(sv != sv2)
+    assert len(bad) == 0, f"{what}: {len(bad)} scale byte mismatches"
+
+
+@pytest.mark.parametrize("block,fmt", [(128, "fp32"), (128, "ue8m0"), (32, "fp32"), (32, "ue8m0"), (32, "e8m0")])
+def test_act_quant_tiny(F, orc, block, fmt):
+    x = W.tiny_linear().x
+    _assert_same(*_run_act(F, orc, x, block, fmt), f"tiny {block} {fmt}")
+
+
+def _edge_rows():
+    """Rows of 128 bf16 values exercising zero blocks, signed zeros,
+    subnormals, ties, saturation of the block maximum and huge values."""
+    rows = []
+    rows.append(np.zeros(128, np.float32))
+    z = np.zeros(128, np.float32); z[::2] = -0.0; rows.append(z)
+    rows.append(np.full(128, 2.0 ** -133, np.float32))                      # bf16 subnormals
+    t = np.linspace(-1, 1, 128).astype(np.float32) * 2.0 ** -130; rows.append(t)
+    rows.append(np.full(128, 3.0e38, np.float32) * np.sign(np.linspace(-1, 1, 128)).astype(np.float32))
+    h = np.zeros(128, np.float32)                                           # hand-worked style ties
+    vals = [896, -896, 2, -2, 1, 6, 0.0078125, 0.001953125, 0.005859375, 832, 864, 2.25, 2.125, 2.375,
+            0.029296875, 0.03125, 640, 12, 0.25, 100, 3, 5, 7, 9]
+    h[:len(vals)] = vals; rows.append(h)
+    rng = np.random.default_rng(5)
+    for scale in (1e-3, 1.0, 1e3, 2.0 ** 100, 2.0 ** -100):
+        rows.append((rng.standard_normal(128) * scale).astype(np.float32))
+    o = rng.standard_normal(128).astype(np.float32); o[17] = 1e4; rows.append(o)  # one outlier
+    x = torch.from_numpy(np.stack(rows)).to(torch.bfloat16)
+    return x
+
+
+@pytest.mark.parametrize("block,fmt", [(128, "fp32"), (128, "ue8m0"), (32, "fp32"), (32, "e8m0")])
+def test_act_quant_edge_cases(F, orc, block, fmt):
+    x = _edge_rows()
+    _assert_same(*_run_act(F, orc, x, block, fmt), f"edge {block} {fmt}")
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 256), (5, 7168), (33, 384)])
+def test_act_quant_ragged_shapes(F, orc, M, K):
+    g = W.gen(11 + M)
+    x = W.activations(M, K, 1, 30.0, g)
+    _assert_same(*_run_act(F, orc, x, 128, "fp32"), f"{M}x{K}")
+
+
+def test_act_quant_strided_rows(F, orc):
+    """ld_x > K and ld_q > K: only the first K columns are read/written."""
+    g = W.gen(3)
+    big = W.activations(40, 512, 2, 25.0, g).to(DEV)
+    x = big[:, :384]
+    q = torch.full((40, 400), 0xAB, dtype=torch.uint8, device=DEV)
+    s = torch.empty(40, 3, dtype=torch.float32, device=DEV)
+    F.fp8_act_quant(x, 128, "fp32", q=q[:, :384], scales=s)
+    torch.cuda.synchronize()
+    q2, s2 = orc.act_quant(W.bits(x.cpu()), 128, 0)
+    qn = _np(q)
+    assert (qn[:, 384:] == 0xAB).all()
+    _assert_same(qn[:, :384], _np(s), q2, s2, "strided")
+
+
+def test_act_quant_decode_full(F, orc):
+    c = W.decode_linear(device=DEV)
+    for M in (1, 8, 32, 128):
+        _assert_same(*_run_act(F, orc, c.x[:M], 128, "ue8m0"), f"decode M={M}")
+
+
+def test_act_quant_prefill_full(F, orc):
+    c = W.prefill_linear(device=DEV)
+    _assert_same(*_run_act(F, orc, c.x, 128, "fp32"), "prefill 4096x7168")
+
+
+def test_act_quant_mx_operand_full(F, orc):
+    a, _ = W.mx_case(device=DEV, N=128)
+    _assert_same(*_run_act(F, orc, a, 32, "e8m0"), "mx 8192x8192")
+
+
+def test_act_quant_deterministic(F):
+    c = W.prefill_linear(device=DEV, M=512)
+    q1, s1 = F.fp8_act_quant(c.x, 128, "fp32")
+    q2, s2 = F.fp8_act_quant(c.x, 128, "fp32")
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
+def test_weight_quant_tiny_and_outlier(F, orc, fmt):
+    g = W.gen(21)
+    w = W.weights(384, 512, 0.02, g)
+    w[3, 200] = 1.5
+    w[300, 7] = -40.0
+    wq, ws = F.fp8_weight_quant(w.to(DEV), fmt)
+    torch.cuda.synchronize()
+    q2, s2 = orc.weight_quant(W.bits(w), {"fp32": 0, "ue8m0": 1}[fmt])
+    _assert_same(_np(wq), _np(ws), q2, s2, f"weight {fmt}")
+
+
+def test_weight_quant_prefill_full(F, orc):
+    c = W.prefill_linear(device=DEV)
+    wq, ws = F.fp8_weight_quant(c.w, "fp32")
+    torch.cuda.synchronize()
+    q2, s2 = orc.weight_quant(W.bits(c.w), 0)
+    _assert_same(_np(wq), _np(ws), q2, s2, "weight 18432x7168")
+
+
+def test_weight_quant_decode_sampled(F, orc):
+    c = W.decode_linear(device=DEV)
+    wq, ws = F.fp8_weight_quant(c.w, "ue8m0")
+    torch.cuda.synchronize()
+    for r0 in (0, 14336, 28672 - 1024):           # 128-row blocks are independent
+        q2, s2 = orc.weight_quant(W.bits(c.w[r0:r0 + 1024]), 1)
+        _assert_same(_np(wq[r0:r0 + 1024]), _np(ws[r0 // 128:(r0 + 1024) // 128]), q2, s2, f"weight rows {r0}")
+
+
+def _cast_inputs():
+    """fp32 patterns: every exponent, mantissas at and around every E4M3 and
+    E5M2 rounding boundary, both signs, plus random patterns."""
+    pats = []
+    hi = np.arange(0, 256, dtype=np.uint32)          # sign+exponent byte
+    lows = np.array([0, 1, 2, 0x7FFF, 0x8000, 0x8001, 0x7FFFF, 0x80000, 0x80001, 0xFFFFF, 0x100000,
+                     0x100001, 0x3FFFFF, 0x400000, 0x400001, 0x7FFFFF], np.uint32)
+    top = np.arange(0, 8, dtype=np.uint32) << 20     # the 3 mantissa bits E4M3 keeps
+    for h in hi:
+        for t in top:
+            pats.append((h << 23) | t | lows)
+            pats.append(((h | 0x100) << 23) | t | lows)   # negative
+    pats.append(np.random.default_rng(9).integers(0, 2 ** 32, size=1 << 22, dtype=np.uint64).astype(np.uint32))
+    u = np.concatenate(pats).astype(np.uint32)
+    v = u.view(np.float32)
+    return v[~np.isnan(v)]
+
+
+def test_cast_e4m3_e5m2(F, orc):
+    v = _cast_inputs()
+    x = torch.from_numpy(v).to(DEV)
+    for fmt, enc in ((F.FMT_E4M3, orc.e4m3_encode), (F.FMT_E5M2, orc.e5m2_encode)):
+        q = _np(F.fp8_cast_f32(x, fmt))
+        want = enc(v)
+        bad = np.argwhere(q != want)
+        assert len(bad) == 0, f"fmt {fmt}: {len(bad)} mismatches, first v={v[bad[0][0]]!r} ({v.view(np.uint32)[bad[0][0]]:#010x}) gpu {q[bad[0][0]]:#x} oracle {want[bad[0][0]]:#x}"
