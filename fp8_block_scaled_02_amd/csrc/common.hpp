@@ -5,11 +5,9 @@
 
 namespace fp8blk {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-
-// E8M0 byte meaning 2^0 for the scaled MFMA (exponent bias 127).
-constexpr int kUnitScale = 127;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
   return __uint_as_float(b16 << 16);

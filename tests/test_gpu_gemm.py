@@ -201,3 +201,34 @@ def test_grouped_full_sampled(F, orc):
     yg, yr, bnd = _moe_run(F, orc, case, rows=rows)
     worst = assert_parity(yg, yr, bnd, True, "moe 256 experts")
     print(f"moe full worst {worst:.3g}; rows {rows}")
+
+
+def test_block_gemm_decodes_every_code_exactly(F, orc):
+    """W = identity (code for 1.0 on the diagonal), unit scales: y[m][n] is
+    the value of a[m][n], for all 254 finite E4M3 codes."""
+    tab = orc.e4m3_table()
+    codes = np.array([c for c in range(256) if np.isfinite(tab[c])], np.uint8)
+    a = np.zeros((2, 128), np.uint8)
+    a.reshape(-1)[:len(codes)] = codes
+    w = np.zeros((128, 128), np.uint8)
+    np.fill_diagonal(w, int(orc.e4m3_encode(np.array([1.0], np.float32))[0]))
+    ta, tw = torch.from_numpy(a).to(DEV), torch.from_numpy(w).to(DEV)
+    one = torch.ones(2, 1, dtype=torch.float32, device=DEV)
+    y = F.fp8_block_gemm(ta, one, tw, torch.ones(1, 1, dtype=torch.float32, device=DEV), torch.float32)
+    np.testing.assert_array_equal(_np(y), tab[a])
+
+
+def test_mx_gemm_applies_block_exponents_exactly(F, orc):
+    """Identity B with byte 127; A codes with E8M0 bytes 117..137 per 32-block:
+    y = value(a) * 2^(e - 127) exactly."""
+    tab = orc.e4m3_table()
+    rng = np.random.default_rng(8)
+    a = rng.integers(0, 0x7E, size=(8, 128)).astype(np.uint8)
+    a[:, ::3] |= 0x80
+    ea = rng.integers(117, 138, size=(8, 4)).astype(np.uint8)
+    b = np.zeros((128, 128), np.uint8)
+    np.fill_diagonal(b, int(orc.e4m3_encode(np.array([1.0], np.float32))[0]))
+    eb = np.full((128, 4), 127, np.uint8)
+    y = F.mxfp8_gemm(*[torch.from_numpy(v).to(DEV) for v in (a, ea, b, eb)])
+    want = tab[a] * np.ldexp(1.0, np.repeat(ea.astype(int) - 127, 32, axis=1))
+    np.testing.assert_array_equal(_np(y), want)
