@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
     p.add_argument("--only", default="", help="run one leg only: decode|mx|moe|prefill")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy (a kernel of known traffic, for "
+                        "scaling profiler byte counters)")
     return p.parse_args()
 
 
@@ -58,17 +61,25 @@ def kernel_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(name, launches_per_record=1):
-    """HBM traffic of one launch from the committed rocprofv3 counter summary,
-    or None if it is missing or was taken on different kernel sources."""
-    path = os.path.join(HERE, "profiles", f"traffic_{name}.json")
+def load_traffic(name):
+    """HBM bytes of one launch from the committed rocprofv3 counter summary
+    (profiles/traffic_<name>.txt, "key: value" lines), or None if it is
+    missing or was taken on different kernel sources."""
+    path = os.path.join(HERE, "profiles", f"traffic_{name}.txt")
     if not os.path.exists(path):
         return None
+    rec = {}
     with open(path) as f:
-        rec = json.load(f)
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
     if rec.get("kernel_hash") != kernel_hash():
         return None
-    return rec.get("bytes_per_launch")
+    try:
+        return int(float(rec["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def timed(torch, fn, iters):
@@ -170,6 +181,15 @@ def main():
 
     del x, a, sa, y, wq, ws
     torch.cuda.empty_cache()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
 
     if not args.no_legs:
         legs.update(run_legs(torch, F, W, dev, args.only))
