@@ -73,4 +73,34 @@ __device__ __forceinline__ float clamp448(float v) {
   return fminf(fmaxf(v, -448.0f), 448.0f);
 }
 
+// Division by a block scale d = fp32(amax / 448), correctly rounded like
+// the IEEE quotient x / d, at a fraction of its cost.  Per block: y = 1 / d
+// (one IEEE division).  Per element: q = x * y, one residual r = x - q * d
+// (exact with FMA) and one correction q + r * y (Markstein's method for a
+// correctly rounded reciprocal), then the sign of x restored (the
+// correction turns (-0) into +0).  Blocks with amax < 2^-62 would put the
+// residual below fp32's normal range and use the IEEE division instead.
+// Verified exhaustively on gfx950: for every positive finite bf16 amax and
+// every bf16 x with |x| <= amax, the E4M3 code of the clamped quotient is
+// identical to the one from the IEEE division.
+struct BlockDivisor {
+  float d, y;
+  bool fast;
+};
+
+__device__ __forceinline__ BlockDivisor make_divisor(float amax, float d) {
+  BlockDivisor b;
+  b.d = d;
+  b.fast = amax >= 0x1.0p-62f;
+  b.y = 1.0f / d;
+  return b;
+}
+
+__device__ __forceinline__ float divide(float x, const BlockDivisor& b) {
+  if (!b.fast) return x / b.d;
+  const float q = x * b.y;
+  const float r = __builtin_fmaf(-q, b.d, x);
+  return copysignf(__builtin_fmaf(r, b.y, q), x);
+}
+
 }  // namespace fp8blk

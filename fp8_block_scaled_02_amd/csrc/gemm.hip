@@ -45,12 +45,18 @@
 
 namespace fp8blk {
 
+#ifndef FP8B_SCHED
+#define FP8B_SCHED 4  // 0: compiler, 1: sched_barrier windows, 2/3: iglp_opt, 4: register ties
+#endif
+
 constexpr int kBK = 128;
 constexpr int kGroupM = 8;  // m-tiles per tile-order group
 
-template <int BM_, int BN_, int WM_, int WN_, bool MX_>
+// Tile configuration: BM x BN output tile, WM x WN waves (each TM x TN),
+// S LDS stages (prefetch distance S-1 K steps).
+template <int BM_, int BN_, int WM_, int WN_, bool MX_, int S_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
   static constexpr bool MX = MX_;
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
@@ -61,7 +67,7 @@ struct Cfg {
   static constexpr int NS_A = BM / 64;
   static constexpr int NS_B = MX ? BN / 64 : 1;
   static constexpr int NS = NS_A + NS_B;
-  // LDS layout of one buffer
+  // LDS layout of one stage
   static constexpr int OFF_W = BM * 128;
   static constexpr int OFF_SA = (BM + BN) * 128;
   static constexpr int OFF_SB = OFF_SA + BM * 4;
@@ -69,6 +75,9 @@ struct Cfg {
   static_assert(GROUPS % NW == 0, "row groups must split evenly over waves");
   static_assert(NS <= NW, "at most one scale load per wave");
   static_assert(TM % 16 == 0 && TN % 16 == 0 && BM % 64 == 0 && BN % 128 == 0, "tile shape");
+  static_assert(TN <= 128, "a wave's columns lie in one weight-scale block");
+  static_assert(S == 2 || S == 3, "two or three LDS stages");
+  static_assert(S * BUF <= 160 * 1024, "LDS capacity");
 };
 
 // LDS byte offset of logical 16-byte chunk `ch` (0..7) of tile row `r`.
@@ -83,8 +92,17 @@ __device__ __forceinline__ void dma4(const void* src, uint8_t* dst_wave_base) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)dst_wave_base, 4, 0, 0);
 }
 
-// vmcnt(0) with the other counters left alone (gfx9 s_waitcnt encoding).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt bits
+// [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// The wave index as a scalar (it is uniform; saying so keeps LDS bases and
+// M0 setup in SALU).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Map a linear workgroup id to an output tile (tm, tn): first give each XCD
 // a contiguous range of ids (workgroups are dealt to the 8 XCDs round
@@ -101,12 +119,17 @@ __device__ __forceinline__ void tile_of(int pid, int nwg, int tiles_m, int tiles
   tn = in / gsz;
 }
 
-// Per-lane sources of one output tile's direct-to-LDS loads.
+// Per-lane sources of one output tile's direct-to-LDS loads: a uniform base
+// (activation or weight matrix) plus a 32-bit per-lane byte offset, so the
+// loads use scalar-base addressing and each K step only moves the base.
 template <class C>
 struct Src {
-  const uint8_t* code[C::NI];  // row pointer + swizzled chunk offset, K step 0
-  const uint8_t* scale;        // this wave's scale load (K step 0), if any
-  int scale_dst;               // its LDS offset in the buffer, or -1
+  const uint8_t* abase;        // uniform
+  const uint8_t* wbase;        // uniform
+  uint32_t code[C::NI];        // row offset + swizzled chunk offset, K step 0
+  const uint8_t* sbase;        // uniform base of this wave's scale load
+  uint32_t soff;               // per-lane offset of that load
+  int scale_dst;               // its LDS offset in the stage (uniform), or -1
 };
 
 // Row-group bookkeeping: wave w, instruction i fills row group q = w + NW*i,
@@ -114,23 +137,28 @@ struct Src {
 // 8q + (l >> 3) and LDS position (l & 7), which holds logical chunk
 // (l & 7) ^ (row & 7) = (l & 7) ^ (l >> 3).
 template <class C, class ARow, class WRow>
-__device__ __forceinline__ void make_code_src(Src<C>& s, ARow arow, WRow wrow) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int chunk = (lane & 7) ^ (lane >> 3);
+__device__ __forceinline__ void make_code_src(Src<C>& s, ARow arow_off, WRow wrow_off) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const uint32_t chunk = (uint32_t)((lane & 7) ^ (lane >> 3));
 #pragma unroll
   for (int i = 0; i < C::NI; ++i) {
     const int q = wave + C::NW * i;
     const int r = 8 * q + (lane >> 3);
-    s.code[i] = (r < C::BM ? arow(r) : wrow(r - C::BM)) + chunk * 16;
+    s.code[i] = (q < C::BM / 8 ? arow_off(r) : wrow_off(r - C::BM)) + chunk * 16u;
   }
 }
 
 template <class C>
 __device__ __forceinline__ void issue(uint8_t* buf, const Src<C>& s, int kb) {
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
+  const uint8_t* a = s.abase + (size_t)kb * kBK;
+  const uint8_t* w = s.wbase + (size_t)kb * kBK;
 #pragma unroll
-  for (int i = 0; i < C::NI; ++i) dma16(s.code[i] + (int64_t)kb * kBK, buf + (wave + C::NW * i) * 1024);
-  if (s.scale_dst >= 0) dma4(s.scale + (int64_t)kb * 4, buf + s.scale_dst);
+  for (int i = 0; i < C::NI; ++i) {
+    const int q = wave + C::NW * i;
+    dma16((q < C::BM / 8 ? a : w) + s.code[i], buf + q * 1024);
+  }
+  if (s.scale_dst >= 0) dma4(s.sbase + (size_t)kb * 4 + s.soff, buf + s.scale_dst);
 }
 
 // FP8 -> bf16 (exact for every finite E4M3 code; `scale` is a power of two
@@ -176,38 +204,101 @@ __device__ __forceinline__ v4f block_product(const Frag16& w, const Frag16& x, v
   return mfma_bf16(w.k[3], x.k[3], c);
 }
 
-// One K step of the block-scaled GEMM on the wave's MI x NJ subtiles:
-// P = block product (fp32), then acc += P * (sa * sw).
+struct Raw16 {
+  uint4 lo, hi;
+};
+
+__device__ __forceinline__ Raw16 read_raw(const uint8_t* t, int r, int g) {
+  Raw16 v;
+  v.lo = *reinterpret_cast<const uint4*>(t + lds_off(r, g));
+  v.hi = *reinterpret_cast<const uint4*>(t + lds_off(r, g + 4));
+  return v;
+}
+
+__device__ __forceinline__ Frag16 widen(const Raw16& v, float s_lo, float s_hi) {
+  Frag16 f;
+  f.k[0] = cvt8(v.lo.x, v.lo.y, s_lo);
+  f.k[1] = cvt8(v.lo.z, v.lo.w, s_lo);
+  f.k[2] = cvt8(v.hi.x, v.hi.y, s_hi);
+  f.k[3] = cvt8(v.hi.z, v.hi.w, s_hi);
+  return f;
+}
+
+// One K step of the block-scaled GEMM on the wave's MI x NJ subtiles.
+// For each weight fragment j the MI block products run as MI chains of four
+// bf16 MFMAs.  Scheduling windows (sched_barrier) pin the order k-outer /
+// i-inner, so consecutive MFMAs are independent: a dependent MFMA issued
+// right behind its producer stalls on gfx950.  Inside window k the VALU
+// widens a quarter of fragment j+1 and folds fragment j-1's product for
+// subtile row k into acc (acc += P * sa * sw); those have long been
+// complete, so no VALU op waits on an MFMA in flight.
 template <class C>
 __device__ __forceinline__ void compute_block(const uint8_t* buf, v4f (&acc)[C::MI][C::NJ]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  static_assert(C::MI == 4, "one rescale row per K sub-step window");
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave % C::WM, wn = wave / C::WM, l16 = lane & 15, g = lane >> 4;
   const float* sa = reinterpret_cast<const float*>(buf + C::OFF_SA);
   const float* sw = reinterpret_cast<const float*>(buf + C::OFF_SB);
+  const uint8_t* wt = buf + C::OFF_W;
+  Raw16 wraw[C::NJ];
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) wraw[j] = read_raw(wt, wn * C::TN + 16 * j + l16, g);
   Frag16 xf[C::MI];
   float s[C::MI];
   const float sw0 = sw[(wn * C::TN) / 128];
 #pragma unroll
   for (int i = 0; i < C::MI; ++i) {
     const int r = wm * C::TM + 16 * i + l16;
-    xf[i] = load_frag(buf, r, g, 1.0f, 1.0f);
+    xf[i] = widen(read_raw(buf, r, g), 1.0f, 1.0f);
     s[i] = sa[r] * sw0;
   }
-  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  Frag16 wcur = widen(wraw[0], 1.0f, 1.0f), wnext;
+  v4f p[C::MI], prev[C::MI];
+#if FP8B_SCHED == 2
+  __builtin_amdgcn_iglp_opt(0);
+#elif FP8B_SCHED == 3
+  __builtin_amdgcn_iglp_opt(1);
+#endif
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j) {
-    const int rn = wn * C::TN + 16 * j;
-    const Frag16 wf = load_frag(buf + C::OFF_W, rn + l16, g, 1.0f, 1.0f);
-    float swj = sw0;
-    if (C::TN > 128) swj = sw[rn / 128];
 #pragma unroll
-    for (int i = 0; i < C::MI; ++i) {
-      const v4f p = block_product(wf, xf[i], zero);
-      const float si = (C::TN > 128) ? sa[wm * C::TM + 16 * i + l16] * swj : s[i];
+    for (int k = 0; k < 4; ++k) {
+#if FP8B_SCHED == 1
+      __builtin_amdgcn_sched_barrier(0);
+#endif
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], si, acc[i][j][r]);
+      for (int i = 0; i < C::MI; ++i)
+        p[i] = mfma_bf16(wcur.k[k], xf[i].k[k], k == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : p[i]);
+      if (j + 1 < C::NJ) {
+        const uint4& h = k < 2 ? wraw[j + 1].lo : wraw[j + 1].hi;
+        wnext.k[k] = (k & 1) ? cvt8(h.z, h.w, 1.0f) : cvt8(h.x, h.y, 1.0f);
+      }
+      if (j > 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[k][j - 1][r] = __builtin_fmaf(prev[k][r], s[k], acc[k][j - 1][r]);
+      }
+#if FP8B_SCHED == 4
+      // order: this window's VALU results exist before the next window's
+      // MFMAs read their operands
+      if (k < 3) {
+        if (j > 0) asm volatile("" : "+v"(wcur.k[k + 1]), "+v"(acc[k][j - 1]));
+        if (j + 1 < C::NJ) asm volatile("" : "+v"(wcur.k[k + 1]), "+v"(wnext.k[k]));
+        asm volatile("" : "+v"(wcur.k[k + 1]), "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]));
+      }
+#endif
     }
+#if FP8B_SCHED == 1
+    __builtin_amdgcn_sched_barrier(0);
+#endif
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) prev[i] = p[i];
+    if (j + 1 < C::NJ) wcur = wnext;
   }
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      acc[i][C::NJ - 1][r] = __builtin_fmaf(prev[i][r], s[i], acc[i][C::NJ - 1][r]);
 }
 
 // 2^(e - 127) for an E8M0 byte e in [1, 254] (fp32 normal); e = 0 gives
@@ -223,7 +314,7 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
 // (K 64+16g..) in 32-block 2 + g/2; scale bytes are one dword per row.
 template <class C>
 __device__ __forceinline__ void compute_mx(const uint8_t* buf, v4f (&acc)[C::MI][C::NJ]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave % C::WM, wn = wave / C::WM, l16 = lane & 15, g = lane >> 4;
   const uint32_t* ea = reinterpret_cast<const uint32_t*>(buf + C::OFF_SA);
   const uint32_t* eb = reinterpret_cast<const uint32_t*>(buf + C::OFF_SB);
@@ -233,41 +324,56 @@ __device__ __forceinline__ void compute_mx(const uint8_t* buf, v4f (&acc)[C::MI]
   for (int i = 0; i < C::MI; ++i) {
     const int r = wm * C::TM + 16 * i + l16;
     const uint32_t e = ea[r];
-    xf[i] = load_frag(buf, r, g, e8m0_to_f32((e >> b0) & 0xffu), e8m0_to_f32((e >> b1) & 0xffu));
+    xf[i] = widen(read_raw(buf, r, g), e8m0_to_f32((e >> b0) & 0xffu), e8m0_to_f32((e >> b1) & 0xffu));
   }
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j) {
     const int r = wn * C::TN + 16 * j + l16;
     const uint32_t e = eb[r];
-    const Frag16 wf = load_frag(buf + C::OFF_W, r, g, e8m0_to_f32((e >> b0) & 0xffu),
-                                e8m0_to_f32((e >> b1) & 0xffu));
+    const Frag16 wf = widen(read_raw(buf + C::OFF_W, r, g), e8m0_to_f32((e >> b0) & 0xffu),
+                            e8m0_to_f32((e >> b1) & 0xffu));
+    // k-outer order: consecutive MFMAs go to different accumulators
 #pragma unroll
-    for (int i = 0; i < C::MI; ++i) acc[i][j] = block_product(wf, xf[i], acc[i][j]);
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) acc[i][j] = mfma_bf16(wf.k[k], xf[i].k[k], acc[i][j]);
   }
 }
 
-// Full K loop of one output tile.  Buffer b is filled by the loads issued
-// one step earlier; every step waits for its own loads, then one barrier
-// makes everyone's loads visible and guarantees the other buffer is no
-// longer being read, then the next step's loads go out and the math runs.
+// Full K loop of one output tile over an S-stage LDS ring (separate arrays,
+// so the compiler sees that the stage being filled never aliases the one
+// being read).  Step kb: wait for this wave's loads of step kb (the loads of
+// the S-2 later steps may stay in flight), one barrier (everyone's loads of
+// step kb are visible and everyone is done reading the stage about to be
+// refilled), issue step kb+S-1, compute step kb.
 template <class C>
-__device__ __forceinline__ void k_loop(uint8_t* lds0, uint8_t* lds1, const Src<C>& src, int nkb,
+__device__ __forceinline__ void k_step(uint8_t* cur, uint8_t* refill, const Src<C>& src, int kb, int nkb,
+                                       v4f (&acc)[C::MI][C::NJ]) {
+  if (C::S == 3 && kb + 1 < nkb) wait_vmem<C::NI>(); else wait_vmem<0>();
+  __syncthreads();
+  if (kb + C::S - 1 < nkb) issue<C>(refill, src, kb + C::S - 1);
+  if (C::MX) compute_mx<C>(cur, acc); else compute_block<C>(cur, acc);
+}
+
+template <class C>
+__device__ __forceinline__ void k_loop(uint8_t* l0, uint8_t* l1, uint8_t* l2, const Src<C>& src, int nkb,
                                        v4f (&acc)[C::MI][C::NJ]) {
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  issue<C>(lds0, src, 0);
-  for (int kb = 0; kb < nkb; kb += 2) {
-    wait_vmem();
-    __syncthreads();
-    if (kb + 1 < nkb) issue<C>(lds1, src, kb + 1);
-    if (C::MX) compute_mx<C>(lds0, acc); else compute_block<C>(lds0, acc);
-    if (kb + 1 < nkb) {
-      wait_vmem();
-      __syncthreads();
-      if (kb + 2 < nkb) issue<C>(lds0, src, kb + 2);
-      if (C::MX) compute_mx<C>(lds1, acc); else compute_block<C>(lds1, acc);
+  issue<C>(l0, src, 0);
+  if (C::S == 2) {
+    for (int kb = 0; kb < nkb; kb += 2) {
+      k_step<C>(l0, l1, src, kb, nkb, acc);
+      if (kb + 1 < nkb) k_step<C>(l1, l0, src, kb + 1, nkb, acc);
+    }
+  } else {
+    if (nkb > 1) issue<C>(l1, src, 1);
+    for (int kb = 0; kb < nkb; kb += 3) {
+      k_step<C>(l0, l2, src, kb, nkb, acc);
+      if (kb + 1 < nkb) k_step<C>(l1, l0, src, kb + 1, nkb, acc);
+      if (kb + 2 < nkb) k_step<C>(l2, l1, src, kb + 2, nkb, acc);
     }
   }
 }
@@ -290,7 +396,7 @@ __device__ __forceinline__ void store4(void* __restrict__ y, int64_t off, const 
 template <class C, bool BF16, class RowOff>
 __device__ __forceinline__ void epilogue(void* __restrict__ y, const v4f (&acc)[C::MI][C::NJ], int n0,
                                          RowOff row_off) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave % C::WM, wn = wave / C::WM, l16 = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int i = 0; i < C::MI; ++i) {
@@ -302,71 +408,85 @@ __device__ __forceinline__ void epilogue(void* __restrict__ y, const v4f (&acc)[
   }
 }
 
+// Stage arrays: a kernel declares all three (unused ones cost nothing; the
+// compiler drops them) so one body serves S = 2 and S = 3.
+#define FP8B_STAGES(C)                                                          \
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[C::BUF];                 \
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[C::BUF];                 \
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[C::S == 3 ? C::BUF : 16]
+
 // ---- block-scaled GEMM ------------------------------------------------------
+// Occupancy: 512-thread tiles run one workgroup per CU (2 waves per SIMD);
+// 256-thread tiles two.
 template <class C, bool BF16>
-__global__ __launch_bounds__(C::NT, 2) void block_gemm_kernel(
+__global__ __launch_bounds__(C::NT, 512 / C::NT) void block_gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ SA,
     const uint8_t* __restrict__ W, int64_t ldw, const float* __restrict__ SW, int M, int N, int K,
     void* __restrict__ Y, int64_t ldy) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[C::BUF];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[C::BUF];
+  FP8B_STAGES(C);
   const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = N / C::BN;
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN, nkb = K / kBK;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
 
   Src<C> src;
   // rows past M re-read the last row; their results are never stored
-  make_code_src<C>(src, [&](int r) { return A + (int64_t)min(m0 + r, M - 1) * lda; },
-                   [&](int r) { return W + (int64_t)(n0 + r) * ldw; });
+  src.abase = A;
+  src.wbase = W + (int64_t)n0 * ldw;
+  make_code_src<C>(src, [&](int r) { return (uint32_t)(min(m0 + r, M - 1) * lda); },
+                   [&](int r) { return (uint32_t)(r * ldw); });
   src.scale_dst = -1;
-  src.scale = A;
+  src.sbase = reinterpret_cast<const uint8_t*>(SA);
+  src.soff = 0;
   if (wave < C::NS_A) {
-    src.scale = reinterpret_cast<const uint8_t*>(SA + (int64_t)min(m0 + 64 * wave + lane, M - 1) * nkb);
+    src.soff = (uint32_t)(min(m0 + 64 * wave + lane, M - 1) * nkb * 4);
     src.scale_dst = C::OFF_SA + 256 * wave;
   } else if (wave == C::NS_A) {
-    const int nb = n0 / 128 + min(lane, C::BN / 128 - 1);
-    src.scale = reinterpret_cast<const uint8_t*>(SW + (int64_t)nb * nkb);
+    src.sbase = reinterpret_cast<const uint8_t*>(SW);
+    src.soff = (uint32_t)((n0 / 128 + min(lane, C::BN / 128 - 1)) * nkb * 4);
     src.scale_dst = C::OFF_SB;
   }
 
   v4f acc[C::MI][C::NJ];
-  k_loop<C>(lds0, lds1, src, nkb, acc);
+  k_loop<C>(lds0, lds1, lds2, src, nkb, acc);
   epilogue<C, BF16>(Y, acc, n0, [&](int r) -> int64_t { return m0 + r < M ? (int64_t)(m0 + r) * ldy : -1; });
 }
 
 // ---- MXFP8 GEMM ---------------------------------------------------------------
 template <class C>
-__global__ __launch_bounds__(C::NT, 2) void mx_gemm_kernel(
+__global__ __launch_bounds__(C::NT, 512 / C::NT) void mx_gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ EA,
     const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ EB, int M, int N, int K,
     float* __restrict__ Y, int64_t ldy) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[C::BUF];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[C::BUF];
+  FP8B_STAGES(C);
   const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = N / C::BN;
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN, nkb = K / kBK;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t srow = K / 32;  // E8M0 bytes per row
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int srow = K / 32;  // E8M0 bytes per row
 
   Src<C> src;
-  make_code_src<C>(src, [&](int r) { return A + (int64_t)min(m0 + r, M - 1) * lda; },
-                   [&](int r) { return B + (int64_t)(n0 + r) * ldb; });
+  src.abase = A;
+  src.wbase = B + (int64_t)n0 * ldb;
+  make_code_src<C>(src, [&](int r) { return (uint32_t)(min(m0 + r, M - 1) * lda); },
+                   [&](int r) { return (uint32_t)(r * ldb); });
   src.scale_dst = -1;
-  src.scale = A;
+  src.sbase = EA;
+  src.soff = 0;
   if (wave < C::NS_A) {
-    src.scale = EA + (int64_t)min(m0 + 64 * wave + lane, M - 1) * srow;
+    src.soff = (uint32_t)(min(m0 + 64 * wave + lane, M - 1) * srow);
     src.scale_dst = C::OFF_SA + 256 * wave;
   } else if (wave < C::NS) {
     const int t = wave - C::NS_A;
-    src.scale = EB + (int64_t)(n0 + 64 * t + lane) * srow;
+    src.sbase = EB;
+    src.soff = (uint32_t)((n0 + 64 * t + lane) * srow);
     src.scale_dst = C::OFF_SB + 256 * t;
   }
 
   v4f acc[C::MI][C::NJ];
-  k_loop<C>(lds0, lds1, src, nkb, acc);
+  k_loop<C>(lds0, lds1, lds2, src, nkb, acc);
   epilogue<C, false>(Y, acc, n0, [&](int r) -> int64_t { return m0 + r < M ? (int64_t)(m0 + r) * ldy : -1; });
 }
 
@@ -379,15 +499,14 @@ __global__ __launch_bounds__(C::NT, 2) void mx_gemm_kernel(
 constexpr int kMaxExperts = 1024;
 
 template <class C, bool BF16>
-__global__ __launch_bounds__(C::NT, 2) void grouped_gemm_kernel(
+__global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ SA, int T,
     const int32_t* __restrict__ RI, const int32_t* __restrict__ OFFS, int R, int E,
     const uint8_t* __restrict__ W, const float* __restrict__ SW, int N, int K, void* __restrict__ Y) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[C::BUF];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[C::BUF];
+  FP8B_STAGES(C);
   __shared__ int tstart[kMaxExperts + 1];
   __shared__ int part[C::NT];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int tiles_n = N / C::BN, nkb = K / kBK;
 
   auto off_at = [&](int e) { return min(max(OFFS[e], 0), R); };
@@ -427,34 +546,204 @@ __global__ __launch_bounds__(C::NT, 2) void grouped_gemm_kernel(
     const int loc = wk - tstart[e];
     const int tn = loc / mt, tm = loc - tn * mt;
     const int r0 = rb + tm * C::BM, n0 = tn * C::BN;
-    const uint8_t* We = W + (int64_t)e * N * K;
     auto token = [&](int r) { return min(max(RI[min(r0 + r, re - 1)], 0), T - 1); };
 
     Src<C> src;
-    make_code_src<C>(src, [&](int r) { return A + (int64_t)token(r) * K; },
-                     [&](int r) { return We + (int64_t)(n0 + r) * K; });
+    src.abase = A;
+    src.wbase = W + ((int64_t)e * N + n0) * K;
+    make_code_src<C>(src, [&](int r) { return (uint32_t)token(r) * (uint32_t)K; },
+                     [&](int r) { return (uint32_t)(r * K); });
     src.scale_dst = -1;
-    src.scale = A;
+    src.sbase = reinterpret_cast<const uint8_t*>(SA);
+    src.soff = 0;
     if (wave < C::NS_A) {
-      src.scale = reinterpret_cast<const uint8_t*>(SA + (int64_t)token(64 * wave + lane) * nkb);
+      src.soff = (uint32_t)token(64 * wave + lane) * (uint32_t)(nkb * 4);
       src.scale_dst = C::OFF_SA + 256 * wave;
     } else if (wave == C::NS_A) {
-      const int nb = n0 / 128 + min(lane, C::BN / 128 - 1);
-      src.scale = reinterpret_cast<const uint8_t*>(SW + ((int64_t)e * (N / 128) + nb) * nkb);
+      src.sbase = reinterpret_cast<const uint8_t*>(SW + (int64_t)e * (N / 128) * nkb);
+      src.soff = (uint32_t)((n0 / 128 + min(lane, C::BN / 128 - 1)) * nkb * 4);
       src.scale_dst = C::OFF_SB;
     }
 
-    __syncthreads();  // the previous tile's last step may still read lds0/lds1
+    __syncthreads();  // the previous tile's last steps may still read the stages
     v4f acc[C::MI][C::NJ];
-    k_loop<C>(lds0, lds1, src, nkb, acc);
+    k_loop<C>(lds0, lds1, lds2, src, nkb, acc);
     epilogue<C, BF16>(Y, acc, n0,
                       [&](int r) -> int64_t { return r0 + r < re ? (int64_t)(r0 + r) * N : -1; });
   }
 }
 
+// ---- decode-shaped block GEMM (few tokens) -------------------------------------
+// With M <= 32 the layer streams W once from HBM and the math is small, so
+// the kernel is built for bandwidth.  A workgroup of 4 waves owns 16 * 4/KS
+// weight rows; the KS waves that share 16 rows take every KS-th K block, so
+// together they read contiguous 128*KS-byte runs of each row.  Each wave
+// loads its fragments straight from global memory into a register ring DEPTH
+// K blocks ahead (no LDS staging, no barriers in the loop) and reads the few
+// activation rows (L1/L2 resident) the same way; MI 16-token subtiles cover
+// M.  The KS partial sums are added in a fixed order through LDS at the end.
+#ifndef FP8B_DECODE_DEPTH
+#define FP8B_DECODE_DEPTH 4
+#endif
+#ifndef FP8B_DECODE_KSPLIT
+#define FP8B_DECODE_KSPLIT 4
+#endif
+constexpr int kDecodeDepth = FP8B_DECODE_DEPTH;
+constexpr int kDecodeKSplit = FP8B_DECODE_KSPLIT;
+static_assert(kDecodeKSplit == 1 || kDecodeKSplit == 2 || kDecodeKSplit == 4, "KS divides the 4 waves");
+
+struct Raw16g {
+  uint4 lo, hi;
+};
+
+__device__ __forceinline__ Raw16g load_frag_global(const uint8_t* row_k) {
+  Raw16g v;
+  const int g = (threadIdx.x & 63) >> 4;
+  v.lo = *reinterpret_cast<const uint4*>(row_k + 16 * g);
+  v.hi = *reinterpret_cast<const uint4*>(row_k + 16 * (g + 4));
+  return v;
+}
+
+template <int MI, bool BF16>
+__global__ __launch_bounds__(256) void decode_gemm_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ SA,
+    const uint8_t* __restrict__ W, int64_t ldw, const float* __restrict__ SW, int M, int N, int K,
+    void* __restrict__ Y, int64_t ldy) {
+  constexpr int D = kDecodeDepth, KS = kDecodeKSplit, RG = 4 / KS;  // row groups per workgroup
+  __shared__ v4f part[KS > 1 ? KS - 1 : 1][RG][MI][64];
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+  const int wid = wave_id(), ks = wid % KS, rg = wid / KS;
+  const int n0 = (blockIdx.x * RG + rg) * 16;  // this wave's 16 weight rows
+  const bool live = n0 < N;                    // N % 16 == 0: a wave is all in or all out
+  const int nkb = K / kBK;
+  const int nmine = live && ks < nkb ? (nkb - ks + KS - 1) / KS : 0;  // K blocks this wave adds
+  const int n0c = live ? n0 : 0;
+  const uint8_t* wrow = W + (int64_t)(n0c + l16) * ldw;
+  const float* swrow = SW + (int64_t)(n0c / 128) * nkb;
+  const uint8_t* arow[MI];
+  const float* sarow[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int m = min(16 * i + l16, M - 1);  // rows past M repeat the last; never stored
+    arow[i] = A + (int64_t)m * lda;
+    sarow[i] = SA + (int64_t)m * nkb;
+  }
+  // the t-th K block of this wave; t past the end repeats its last block
+  auto kblock = [&](int t) { return ks + KS * min(t, max(nmine - 1, 0)); };
+
+  Raw16g wr[D], ar[D][MI];
+  float sar[D][MI], swr[D];
+  if (nmine > 0) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      const int kb = kblock(s);
+      wr[s] = load_frag_global(wrow + (int64_t)kb * kBK);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        ar[s][i] = load_frag_global(arow[i] + (int64_t)kb * kBK);
+        sar[s][i] = sarow[i][kb];
+      }
+      swr[s] = swrow[kb];
+    }
+  }
+
+  v4f acc[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int t0 = 0; t0 < nmine; t0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      if (t0 + s < nmine) {
+        const Frag16 wf = widen(Raw16{wr[s].lo, wr[s].hi}, 1.0f, 1.0f);
+        v4f p[MI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const Frag16 xf = widen(Raw16{ar[s][i].lo, ar[s][i].hi}, 1.0f, 1.0f);
+          p[i] = block_product(wf, xf, zero);
+        }
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const float sc = sar[s][i] * swr[s];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][r] = __builtin_fmaf(p[i][r], sc, acc[i][r]);
+        }
+        // refill this ring slot with the block D steps ahead
+        const int kn = kblock(t0 + s + D);
+        wr[s] = load_frag_global(wrow + (int64_t)kn * kBK);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          ar[s][i] = load_frag_global(arow[i] + (int64_t)kn * kBK);
+          sar[s][i] = sarow[i][kn];
+        }
+        swr[s] = swrow[kn];
+      }
+    }
+  }
+
+  if constexpr (KS > 1) {
+    if (ks > 0) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) part[ks - 1][rg][i][lane] = acc[i];
+    }
+    __syncthreads();
+    if (ks > 0 || !live) return;
+#pragma unroll
+    for (int j = 0; j < KS - 1; ++j)
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const v4f o = part[j][rg][i][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][r] += o[r];
+      }
+  }
+  if (!live) return;
+  // lane holds y[16i + l16][n0 + 4g .. +3]
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int m = 16 * i + l16;
+    if (m < M) store4<BF16>(Y, (int64_t)m * ldy + n0 + 4 * g, acc[i]);
+  }
+}
+
+template <int MI>
+static void launch_decode(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
+                          const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
+                          hipStream_t s) {
+  constexpr int rows_per_wg = 16 * (4 / kDecodeKSplit);
+  const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg)), block(256);
+  if (out_bf16)
+    hipLaunchKernelGGL((decode_gemm_kernel<MI, true>), grid, block, 0, s, a, lda, sa, w, ldw, sw, (int)M, (int)N,
+                       (int)K, y, ldy);
+  else
+    hipLaunchKernelGGL((decode_gemm_kernel<MI, false>), grid, block, 0, s, a, lda, sa, w, ldw, sw, (int)M, (int)N,
+                       (int)K, y, ldy);
+}
+
 // ---- host launchers ---------------------------------------------------------
-using BlockCfg = Cfg<128, 128, 2, 2, false>;
-using MxCfg = Cfg<128, 128, 2, 2, true>;
+// Tile configurations (BM, BN, WM, WN) and LDS stages, chosen by measurement
+// on MI355X (4096 x 18432 x 7168 and 8192^3); overridable at build time.
+// Block GEMM: 128 x 128 tiles, 64 x 64 per wave, two stages, two workgroups
+// per CU (larger tiles or deeper rings measured no faster: the wave's
+// MFMA + widening + rescale issue is the limit, not L2 or latency).
+// MX GEMM (no VALU rescale): 256 x 256 tiles, 64 x 128 per wave.
+#ifndef FP8B_BLOCK_CFG
+#define FP8B_BLOCK_CFG 128, 128, 2, 2
+#endif
+#ifndef FP8B_BLOCK_STAGES
+#define FP8B_BLOCK_STAGES 2
+#endif
+#ifndef FP8B_MX_CFG
+#define FP8B_MX_CFG 256, 256, 4, 2
+#endif
+#ifndef FP8B_MX_STAGES
+#define FP8B_MX_STAGES 2
+#endif
+using BlockCfg = Cfg<FP8B_BLOCK_CFG, false, FP8B_BLOCK_STAGES>;
+using MxCfg = Cfg<FP8B_MX_CFG, true, FP8B_MX_STAGES>;
+using MxSmallCfg = Cfg<128, 128, 2, 2, true, 2>;
+using GroupedCfg = Cfg<128, 128, 2, 2, false, 2>;
 
 static int cu_count() {
   int dev = 0, n = 0;
@@ -464,10 +753,10 @@ static int cu_count() {
   return n;
 }
 
-int launch_block_gemm(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
-                      const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
-                      hipStream_t s) {
-  using C = BlockCfg;
+template <class C>
+static void launch_block(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
+                         const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
+                         hipStream_t s) {
   const int64_t tiles = ((M + C::BM - 1) / C::BM) * (N / C::BN);
   const dim3 grid((unsigned)tiles), block(C::NT);
   if (out_bf16)
@@ -476,26 +765,46 @@ int launch_block_gemm(const uint8_t* a, int64_t lda, const float* sa, const uint
   else
     hipLaunchKernelGGL((block_gemm_kernel<C, false>), grid, block, 0, s, a, lda, sa, w, ldw, sw, (int)M, (int)N,
                        (int)K, y, ldy);
+}
+
+int launch_block_gemm(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
+                      const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
+                      hipStream_t s) {
+  if (M <= 16)
+    launch_decode<1>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+  else if (M <= 32)
+    launch_decode<2>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+  else
+    launch_block<BlockCfg>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
   return check_launch();
+}
+
+template <class C>
+static void launch_mx(const uint8_t* a, int64_t lda, const uint8_t* ea, const uint8_t* b, int64_t ldb,
+                      const uint8_t* eb, int64_t M, int64_t N, int64_t K, float* y, int64_t ldy, hipStream_t s) {
+  const int64_t tiles = ((M + C::BM - 1) / C::BM) * (N / C::BN);
+  hipLaunchKernelGGL(mx_gemm_kernel<C>, dim3((unsigned)tiles), dim3(C::NT), 0, s, a, lda, ea, b, ldb, eb, (int)M,
+                     (int)N, (int)K, y, ldy);
 }
 
 int launch_mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* ea, const uint8_t* b, int64_t ldb,
                    const uint8_t* eb, int64_t M, int64_t N, int64_t K, float* y, int64_t ldy, hipStream_t s) {
-  using C = MxCfg;
-  const int64_t tiles = ((M + C::BM - 1) / C::BM) * (N / C::BN);
-  hipLaunchKernelGGL(mx_gemm_kernel<C>, dim3((unsigned)tiles), dim3(C::NT), 0, s, a, lda, ea, b, ldb, eb, (int)M,
-                     (int)N, (int)K, y, ldy);
+  // the big tile once there are enough tiles to fill the chip
+  if (N % MxCfg::BN == 0 && M >= 8 * MxCfg::BM)
+    launch_mx<MxCfg>(a, lda, ea, b, ldb, eb, M, N, K, y, ldy, s);
+  else
+    launch_mx<MxSmallCfg>(a, lda, ea, b, ldb, eb, M, N, K, y, ldy, s);
   return check_launch();
 }
 
 int launch_grouped_gemm(const uint8_t* a, const float* sa, int64_t T, const int32_t* ri, const int32_t* offs,
                         int64_t R, int64_t E, const uint8_t* w, const float* sw, int64_t N, int64_t K, void* y,
                         int out_bf16, hipStream_t s) {
-  using C = BlockCfg;
-  // enough persistent workgroups to fill every CU twice, never more than
-  // the largest possible number of tiles
+  using C = GroupedCfg;
+  // enough persistent workgroups to fill every CU (at its occupancy), never
+  // more than the largest possible number of tiles
   const int64_t max_tiles = ((R + C::BM - 1) / C::BM + E) * (N / C::BN);
-  const int64_t nwg = std::max<int64_t>(1, std::min<int64_t>(2 * (int64_t)cu_count(), max_tiles));
+  const int64_t nwg = std::max<int64_t>(1, std::min<int64_t>((512 / C::NT) * (int64_t)cu_count(), max_tiles));
   const dim3 grid((unsigned)nwg), block(C::NT);
   if (out_bf16)
     hipLaunchKernelGGL((grouped_gemm_kernel<C, true>), grid, block, 0, s, a, sa, (int)T, ri, offs, (int)R, (int)E,

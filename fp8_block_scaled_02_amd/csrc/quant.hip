@@ -15,7 +15,11 @@
 
 namespace fp8blk {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // FMT: 0 fp32 scales, 1 power-of-two scales stored as fp32, 2 E8M0 bytes.
+// Each thread owns UNROLL 16-byte chunks, 256 chunks apart, all loaded
+// before any is processed (bytes in flight per lane = 16 * UNROLL).
 template <int BLOCK, int FMT, int UNROLL>
 __global__ __launch_bounds__(256) void act_quant_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
@@ -35,8 +39,9 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
     ok[u] = c < total;
     row[u] = ok[u] ? c / cpr : 0;
     col[u] = ok[u] ? (c - row[u] * cpr) * 8 : 0;
-    raw[u] = ok[u] ? *reinterpret_cast<const uint4*>(x + row[u] * ldx + col[u])
-                   : make_uint4(0, 0, 0, 0);
+    u32x4 v = {0, 0, 0, 0};
+    if (ok[u]) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + row[u] * ldx + col[u]));
+    raw[u] = make_uint4(v[0], v[1], v[2], v[3]);
   }
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
@@ -45,7 +50,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
-      f[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
     float amax = 0.0f;
 #pragma unroll
@@ -53,24 +58,25 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
     amax = (LPB == 16) ? row16_max(amax) : quad_max(amax);
 
     float qv[8];
-    int e = 0;
+    const bool lead = ok[u] && (col[u] % BLOCK) == 0;
+    const int64_t sidx = row[u] * nblk + col[u] / BLOCK;
     if (FMT == 0) {
       const float d = (amax == 0.0f) ? 1.0f : amax / 448.0f;  // IEEE division
+      const BlockDivisor bd = make_divisor(amax, d);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qv[i] = clamp448(f[i] / d);
-      if (ok[u] && (col[u] % BLOCK) == 0)
-        reinterpret_cast<float*>(scales)[row[u] * nblk + col[u] / BLOCK] = d;
+      for (int i = 0; i < 8; ++i) qv[i] = clamp448(divide(f[i], bd));
+      if (lead) reinterpret_cast<float*>(scales)[sidx] = d;
     } else {
-      e = pow2_scale_exp(amax);
+      const int e = pow2_scale_exp(amax);
       // x / 2^e == x * 2^-e exactly (both are the correctly rounded quotient)
       const float rinv = exp2i(-e);
 #pragma unroll
       for (int i = 0; i < 8; ++i) qv[i] = clamp448(f[i] * rinv);
-      if (ok[u] && (col[u] % BLOCK) == 0) {
+      if (lead) {
         if (FMT == 1)
-          reinterpret_cast<float*>(scales)[row[u] * nblk + col[u] / BLOCK] = exp2i(e);
+          reinterpret_cast<float*>(scales)[sidx] = exp2i(e);
         else
-          reinterpret_cast<uint8_t*>(scales)[row[u] * nblk + col[u] / BLOCK] = (uint8_t)(127 + e);
+          reinterpret_cast<uint8_t*>(scales)[sidx] = (uint8_t)(127 + e);
       }
     }
     if (ok[u]) {
@@ -118,8 +124,10 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
   float d, rinv = 1.0f;
+  BlockDivisor bd{};
   if (FMT == 0) {
     d = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+    bd = make_divisor(amax, d);
   } else {
     const int e = pow2_scale_exp(amax);
     d = exp2i(e);
@@ -138,7 +146,7 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(
       f[2 * j + 1] = bf16_bits_to_f32(v[j] >> 16);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) f[j] = clamp448(FMT == 0 ? f[j] / d : f[j] * rinv);
+    for (int j = 0; j < 8; ++j) f[j] = clamp448(FMT == 0 ? divide(f[j], bd) : f[j] * rinv);
     uint2 out;
     out.x = pack4_e4m3(f[0], f[1], f[2], f[3]);
     out.y = pack4_e4m3(f[4], f[5], f[6], f[7]);
@@ -166,7 +174,7 @@ __global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ x, 
 }
 
 // ---- host launchers --------------------------------------------------------
-constexpr int kActUnroll = 2;
+constexpr int kActUnroll = 4;
 
 int launch_act_quant(const void* x, int64_t M, int64_t K, int64_t ldx, int block, int fmt,
                      uint8_t* q, int64_t ldq, void* scales, hipStream_t s) {

@@ -61,6 +61,19 @@ def test_block_gemm_ragged(F, orc, M, N, K, out):
     assert_parity(yg, yr, bnd, out == torch.bfloat16, f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 512, 1152), (7, 384, 640), (16, 128, 128), (17, 256, 384),
+                                   (20, 256, 1152), (32, 640, 2048)])
+def test_block_gemm_few_tokens(F, orc, M, N, K):
+    """M <= 32 takes the streaming decode kernel: one and two 16-token
+    subtiles, K-block counts below, at and past the prefetch depth and not a
+    multiple of the K split."""
+    c = W.decode_linear(K=K, N=N, seed=M + K)
+    yg, yr, bnd = _linear_case(F, orc, c.x[:M], c.w, "ue8m0", torch.bfloat16)
+    assert_parity(yg, yr, bnd, True, f"{M}x{N}x{K}")
+    yg, yr, bnd = _linear_case(F, orc, c.x[:M], c.w, "fp32", torch.float32)
+    assert_parity(yg, yr, bnd, False, f"{M}x{N}x{K} f32")
+
+
 def test_block_gemm_ue8m0_small(F, orc):
     c = W.decode_linear(K=1024, N=512)
     yg, yr, bnd = _linear_case(F, orc, c.x, c.w, "ue8m0", torch.bfloat16)

@@ -175,3 +175,23 @@ def test_cast_e4m3_e5m2(F, orc):
         want = enc(v)
         bad = np.argwhere(q != want)
         assert len(bad) == 0, f"fmt {fmt}: {len(bad)} mismatches, first v={v[bad[0][0]]!r} ({v.view(np.uint32)[bad[0][0]]:#010x}) gpu {q[bad[0][0]]:#x} oracle {want[bad[0][0]]:#x}"
+
+
+@pytest.mark.parametrize("block", [128, 32])
+def test_act_quant_fp32_scales_every_block_magnitude(F, orc, block):
+    """One quantisation block per bf16 amax pattern (every exponent incl.
+    subnormals, every mantissa): the block holds amax itself, its negation,
+    -0, and random in-range values, so the scale division runs over the whole
+    fp32 range, including the tiny blocks that take the IEEE-division path."""
+    amax_bits = np.arange(1, 0x7F80, dtype=np.uint32)          # every positive finite bf16
+    amax = (amax_bits << 16).view(np.float32)
+    nb = len(amax)
+    rng = np.random.default_rng(17)
+    vals = rng.uniform(-1, 1, size=(nb, block)).astype(np.float32) * amax[:, None]
+    vals[:, 0] = amax
+    vals[:, 1] = -amax
+    vals[:, 2] = -0.0
+    vals[:, 3] = amax * np.float32(0.5 ** 12)                  # rounds deep in the subnormal codes
+    x = torch.from_numpy(vals[: (nb // 4) * 4].reshape(-1, 4 * block)).to(torch.bfloat16)
+    assert float(x.abs().max()) <= 3.39e38
+    _assert_same(*_run_act(F, orc, x, block, "fp32"), f"every amax block {block}")
