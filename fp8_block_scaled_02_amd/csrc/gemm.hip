@@ -39,6 +39,7 @@
 //  * Tile order is remapped so that each XCD (8 per chip, each with its own
 //    L2) works on a contiguous, grouped patch of output tiles.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -490,136 +491,152 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void mx_gemm_kernel(
   epilogue<C, false>(Y, acc, n0, [&](int r) -> int64_t { return m0 + r < M ? (int64_t)(m0 + r) * ldy : -1; });
 }
 
-// ---- grouped (MoE) GEMM -----------------------------------------------------
-// Persistent workgroups; the tile map is rebuilt in LDS by every workgroup
-// from expert_offsets (a prefix sum of per-expert tile counts), so the host
-// never reads the routing.  Work ids are ordered (expert, n-tile, m-tile)
-// with m fastest, so concurrently running m-tiles of a heavy expert share
-// that expert's weight tile in L2.
-constexpr int kMaxExperts = 1024;
-
-template <class C, bool BF16>
-__global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
-    const uint8_t* __restrict__ A, const float* __restrict__ SA, int T,
-    const int32_t* __restrict__ RI, const int32_t* __restrict__ OFFS, int R, int E,
-    const uint8_t* __restrict__ W, const float* __restrict__ SW, int N, int K, void* __restrict__ Y) {
-  FP8B_STAGES(C);
-  __shared__ int tstart[kMaxExperts + 1];
-  __shared__ int part[C::NT];
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int tiles_n = N / C::BN, nkb = K / kBK;
-
-  auto off_at = [&](int e) { return min(max(OFFS[e], 0), R); };
-  auto ntiles = [&](int e) { return ((max(off_at(e + 1) - off_at(e), 0) + C::BM - 1) / C::BM) * tiles_n; };
-
-  // tile map: tstart[e] = first work id of expert e
-  const int per = (E + C::NT - 1) / C::NT;
-  const int e0 = min(tid * per, E), e1 = min(e0 + per, E);
-  int local = 0;
-  for (int e = e0; e < e1; ++e) local += ntiles(e);
-  part[tid] = local;
-  __syncthreads();
-  for (int o = 1; o < C::NT; o <<= 1) {
-    const int v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int run = tid ? part[tid - 1] : 0;
-  for (int e = e0; e < e1; ++e) {
-    tstart[e] = run;
-    run += ntiles(e);
-  }
-  if (tid == C::NT - 1) tstart[E] = part[C::NT - 1];
-  __syncthreads();
-  const int total = tstart[E];
-
-  for (int wk = blockIdx.x; wk < total; wk += gridDim.x) {
-    int lo = 0, hi = E;  // largest e with tstart[e] <= wk
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (tstart[mid] <= wk) lo = mid; else hi = mid;
-    }
-    const int e = lo;
-    const int rb = off_at(e), re = off_at(e + 1);
-    const int mt = (re - rb + C::BM - 1) / C::BM;
-    const int loc = wk - tstart[e];
-    const int tn = loc / mt, tm = loc - tn * mt;
-    const int r0 = rb + tm * C::BM, n0 = tn * C::BN;
-    auto token = [&](int r) { return min(max(RI[min(r0 + r, re - 1)], 0), T - 1); };
-
-    Src<C> src;
-    src.abase = A;
-    src.wbase = W + ((int64_t)e * N + n0) * K;
-    make_code_src<C>(src, [&](int r) { return (uint32_t)token(r) * (uint32_t)K; },
-                     [&](int r) { return (uint32_t)(r * K); });
-    src.scale_dst = -1;
-    src.sbase = reinterpret_cast<const uint8_t*>(SA);
-    src.soff = 0;
-    if (wave < C::NS_A) {
-      src.soff = (uint32_t)token(64 * wave + lane) * (uint32_t)(nkb * 4);
-      src.scale_dst = C::OFF_SA + 256 * wave;
-    } else if (wave == C::NS_A) {
-      src.sbase = reinterpret_cast<const uint8_t*>(SW + (int64_t)e * (N / 128) * nkb);
-      src.soff = (uint32_t)((n0 / 128 + min(lane, C::BN / 128 - 1)) * nkb * 4);
-      src.scale_dst = C::OFF_SB;
-    }
-
-    __syncthreads();  // the previous tile's last steps may still read the stages
-    v4f acc[C::MI][C::NJ];
-    k_loop<C>(lds0, lds1, lds2, src, nkb, acc);
-    epilogue<C, BF16>(Y, acc, n0,
-                      [&](int r) -> int64_t { return r0 + r < re ? (int64_t)(r0 + r) * N : -1; });
-  }
-}
-
-// ---- decode-shaped block GEMM (few tokens) -------------------------------------
-// With M <= 32 the layer streams W once from HBM and the math is small, so
-// the kernel is built for bandwidth.  A workgroup of 4 waves owns 16 * 4/KS
-// weight rows; the KS waves that share 16 rows take every KS-th K block, so
-// together they read contiguous 128*KS-byte runs of each row.  Each wave
-// loads its fragments straight from global memory into a register ring DEPTH
-// K blocks ahead (no LDS staging, no barriers in the loop) and reads the few
-// activation rows (L1/L2 resident) the same way; MI 16-token subtiles cover
-// M.  The KS partial sums are added in a fixed order through LDS at the end.
-#ifndef FP8B_DECODE_DEPTH
-#define FP8B_DECODE_DEPTH 4
-#endif
-#ifndef FP8B_DECODE_KSPLIT
-#define FP8B_DECODE_KSPLIT 4
-#endif
-constexpr int kDecodeDepth = FP8B_DECODE_DEPTH;
-constexpr int kDecodeKSplit = FP8B_DECODE_KSPLIT;
-static_assert(kDecodeKSplit == 1 || kDecodeKSplit == 2 || kDecodeKSplit == 4, "KS divides the 4 waves");
+// ---- streaming few-row block GEMM -------------------------------------------
+// With few activation rows (decode, small MoE experts) a layer streams W once
+// from HBM and the math is small, so this path is built for bandwidth.  A
+// workgroup owns 64 weight rows (4 subtiles of 16 per wave) and up to 16*MI
+// activation rows; its 4 waves take every 4th K block, so together they read
+// contiguous 512-byte runs of each weight row.  Each wave loads its
+// fragments straight from global memory into a register ring kStreamDepth K
+// blocks ahead (no LDS staging, no barrier in the loop); the activation
+// fragments (L2 resident) are loaded once per K block and shared by the 4
+// weight subtiles.  The 4 partial sums are added in a fixed order through
+// LDS at the end.  Measured on MI355X (8192 -> 28672): 64 rows per
+// workgroup beat 16 and 32 by 10-45%, a deeper ring or a 2-way K split was
+// slower, and non-temporal weight loads were 10-15% slower (the two halves
+// of each 128-byte row segment come from different instructions).
+constexpr int kStreamDepth = 2;
+constexpr int kStreamNJ = 4;
+constexpr int kStreamRows = 16 * kStreamNJ;  // weight rows per workgroup
 
 struct Raw16g {
   uint4 lo, hi;
 };
 
+// A lane's 32 codes of one 16-row x 128-K fragment, read from global memory
+// (row_k = this lane's row at the K block).
 __device__ __forceinline__ Raw16g load_frag_global(const uint8_t* row_k) {
-  Raw16g v;
   const int g = (threadIdx.x & 63) >> 4;
+  Raw16g v;
   v.lo = *reinterpret_cast<const uint4*>(row_k + 16 * g);
   v.hi = *reinterpret_cast<const uint4*>(row_k + 16 * (g + 4));
   return v;
 }
 
+// LDS needed by stream_rows<MI>: partial sums of waves 1..3.
+template <int MI>
+constexpr int stream_part_bytes() {
+  return 3 * MI * kStreamNJ * 64 * (int)sizeof(v4f);
+}
+
+// acc[i][j] = y rows 16i + l16 of the chunk, weight rows 16j + 4g .. +3 of
+// the workgroup's 64, over all nkb K blocks.  arow[i] / sarow[i]: this
+// lane's activation row (codes, per-block scales); wrow: this lane's weight
+// row l16 (subtile j at + 16j * ldw); swrow: the weight-scale row of these
+// 64 rows.  Every wave of the workgroup must call it; the sums are complete
+// in wave 0 only (the return value says which), and `part` may be reused by
+// the caller only after a barrier.
+template <int MI>
+__device__ __forceinline__ bool stream_rows(const uint8_t* const (&arow)[MI], const float* const (&sarow)[MI],
+                                            const uint8_t* wrow, int64_t ldw, const float* swrow, int nkb,
+                                            v4f* part, v4f (&acc)[MI][kStreamNJ]) {
+  constexpr int D = kStreamDepth, NJ = kStreamNJ;
+  const int lane = threadIdx.x & 63, ks = wave_id();
+  const int nmine = ks < nkb ? (nkb - ks + 3) / 4 : 0;  // K blocks this wave adds
+  // the t-th K block of this wave; t past the end repeats its last block
+  auto kblock = [&](int t) { return ks + 4 * min(t, max(nmine - 1, 0)); };
+
+  Raw16g wr[D][NJ], ar[D][MI];
+  float sar[D][MI], swr[D];
+  auto fetch = [&](int sl, int kb) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) wr[sl][j] = load_frag_global(wrow + (int64_t)16 * j * ldw + (int64_t)kb * kBK);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      ar[sl][i] = load_frag_global(arow[i] + (int64_t)kb * kBK);
+      sar[sl][i] = sarow[i][kb];
+    }
+    swr[sl] = swrow[kb];
+  };
+  if (nmine > 0) {
+#pragma unroll
+    for (int sl = 0; sl < D; ++sl) fetch(sl, kblock(sl));
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int t0 = 0; t0 < nmine; t0 += D) {
+#pragma unroll
+    for (int sl = 0; sl < D; ++sl) {
+      if (t0 + sl < nmine) {
+        Frag16 xf[MI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) xf[i] = widen(Raw16{ar[sl][i].lo, ar[sl][i].hi}, 1.0f, 1.0f);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const Frag16 wf = widen(Raw16{wr[sl][j].lo, wr[sl][j].hi}, 1.0f, 1.0f);
+#pragma unroll
+          for (int i = 0; i < MI; ++i) {
+            const v4f pr = block_product(wf, xf[i], zero);
+            const float sc = sar[sl][i] * swr[sl];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[r], sc, acc[i][j][r]);
+          }
+        }
+        fetch(sl, kblock(t0 + sl + D));  // refill this slot with the block D steps ahead
+      }
+    }
+  }
+
+  if (ks > 0) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) part[(((ks - 1) * MI + i) * NJ + j) * 64 + lane] = acc[i][j];
+  }
+  __syncthreads();
+  if (ks > 0) return false;
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const v4f o = part[((q * MI + i) * NJ + j) * 64 + lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] += o[r];
+      }
+  return true;
+}
+
+// Lane's outputs of stream_rows: chunk row 16i + l16 at element offset
+// row_off(16i + l16) of y (skipped when negative), columns n0 + 16j + 4g .. +3.
+template <int MI, bool BF16, class RowOff>
+__device__ __forceinline__ void stream_store(void* __restrict__ y, const v4f (&acc)[MI][kStreamNJ], int n0,
+                                             RowOff row_off) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int64_t base = row_off(16 * i + l16);
+    if (base >= 0) {
+#pragma unroll
+      for (int j = 0; j < kStreamNJ; ++j) store4<BF16>(y, base + n0 + 16 * j + 4 * g, acc[i][j]);
+    }
+  }
+}
+
+// Block GEMM for M <= 16*MI: one workgroup per 64 weight rows.
 template <int MI, bool BF16>
 __global__ __launch_bounds__(256) void decode_gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ SA,
     const uint8_t* __restrict__ W, int64_t ldw, const float* __restrict__ SW, int M, int N, int K,
     void* __restrict__ Y, int64_t ldy) {
-  constexpr int D = kDecodeDepth, KS = kDecodeKSplit, RG = 4 / KS;  // row groups per workgroup
-  __shared__ v4f part[KS > 1 ? KS - 1 : 1][RG][MI][64];
-  const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
-  const int wid = wave_id(), ks = wid % KS, rg = wid / KS;
-  const int n0 = (blockIdx.x * RG + rg) * 16;  // this wave's 16 weight rows
-  const bool live = n0 < N;                    // N % 16 == 0: a wave is all in or all out
-  const int nkb = K / kBK;
-  const int nmine = live && ks < nkb ? (nkb - ks + KS - 1) / KS : 0;  // K blocks this wave adds
-  const int n0c = live ? n0 : 0;
-  const uint8_t* wrow = W + (int64_t)(n0c + l16) * ldw;
-  const float* swrow = SW + (int64_t)(n0c / 128) * nkb;
+  __shared__ v4f part[stream_part_bytes<MI>() / sizeof(v4f)];
+  const int l16 = threadIdx.x & 15;
+  const int n0 = blockIdx.x * kStreamRows, nkb = K / kBK;
   const uint8_t* arow[MI];
   const float* sarow[MI];
 #pragma unroll
@@ -628,97 +645,166 @@ __global__ __launch_bounds__(256) void decode_gemm_kernel(
     arow[i] = A + (int64_t)m * lda;
     sarow[i] = SA + (int64_t)m * nkb;
   }
-  // the t-th K block of this wave; t past the end repeats its last block
-  auto kblock = [&](int t) { return ks + KS * min(t, max(nmine - 1, 0)); };
-
-  Raw16g wr[D], ar[D][MI];
-  float sar[D][MI], swr[D];
-  if (nmine > 0) {
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-      const int kb = kblock(s);
-      wr[s] = load_frag_global(wrow + (int64_t)kb * kBK);
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        ar[s][i] = load_frag_global(arow[i] + (int64_t)kb * kBK);
-        sar[s][i] = sarow[i][kb];
-      }
-      swr[s] = swrow[kb];
-    }
-  }
-
-  v4f acc[MI];
-#pragma unroll
-  for (int i = 0; i < MI; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-
-  for (int t0 = 0; t0 < nmine; t0 += D) {
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-      if (t0 + s < nmine) {
-        const Frag16 wf = widen(Raw16{wr[s].lo, wr[s].hi}, 1.0f, 1.0f);
-        v4f p[MI];
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          const Frag16 xf = widen(Raw16{ar[s][i].lo, ar[s][i].hi}, 1.0f, 1.0f);
-          p[i] = block_product(wf, xf, zero);
-        }
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          const float sc = sar[s][i] * swr[s];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][r] = __builtin_fmaf(p[i][r], sc, acc[i][r]);
-        }
-        // refill this ring slot with the block D steps ahead
-        const int kn = kblock(t0 + s + D);
-        wr[s] = load_frag_global(wrow + (int64_t)kn * kBK);
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          ar[s][i] = load_frag_global(arow[i] + (int64_t)kn * kBK);
-          sar[s][i] = sarow[i][kn];
-        }
-        swr[s] = swrow[kn];
-      }
-    }
-  }
-
-  if constexpr (KS > 1) {
-    if (ks > 0) {
-#pragma unroll
-      for (int i = 0; i < MI; ++i) part[ks - 1][rg][i][lane] = acc[i];
-    }
-    __syncthreads();
-    if (ks > 0 || !live) return;
-#pragma unroll
-    for (int j = 0; j < KS - 1; ++j)
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const v4f o = part[j][rg][i][lane];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][r] += o[r];
-      }
-  }
-  if (!live) return;
-  // lane holds y[16i + l16][n0 + 4g .. +3]
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    const int m = 16 * i + l16;
-    if (m < M) store4<BF16>(Y, (int64_t)m * ldy + n0 + 4 * g, acc[i]);
-  }
+  v4f acc[MI][kStreamNJ];
+  if (!stream_rows<MI>(arow, sarow, W + (int64_t)(n0 + l16) * ldw, ldw, SW + (int64_t)(n0 / 128) * nkb, nkb, part,
+                       acc))
+    return;
+  stream_store<MI, BF16>(Y, acc, n0, [&](int r) -> int64_t { return r < M ? (int64_t)r * ldy : -1; });
 }
 
-template <int MI>
-static void launch_decode(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
-                          const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
-                          hipStream_t s) {
-  constexpr int rows_per_wg = 16 * (4 / kDecodeKSplit);
-  const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg)), block(256);
-  if (out_bf16)
-    hipLaunchKernelGGL((decode_gemm_kernel<MI, true>), grid, block, 0, s, a, lda, sa, w, ldw, sw, (int)M, (int)N,
-                       (int)K, y, ldy);
-  else
-    hipLaunchKernelGGL((decode_gemm_kernel<MI, false>), grid, block, 0, s, a, lda, sa, w, ldw, sw, (int)M, (int)N,
-                       (int)K, y, ldy);
+// ---- grouped (MoE) GEMM -----------------------------------------------------
+// Persistent workgroups over two kinds of work item, both mapped in LDS by
+// every workgroup from expert_offsets (prefix sums of per-expert counts), so
+// the host never reads the routing:
+//  * tile items: 128 x 128 output tiles of an expert's rows, ordered
+//    (expert, n-tile, m-tile) with m fastest, so concurrently running m-tiles
+//    of a heavy expert share its weight tile in L2;
+//  * stream items: an expert's last (rows mod 128) rows when there are at
+//    most kStreamTail of them (most experts of a skewed routing have only a
+//    few rows): 64 weight rows each, on the streaming path, so a 5-row
+//    expert costs one pass over its weights instead of 128-row tiles of MFMA
+//    work.
+// Tile items come first and the fine-grained stream items fill the end of the
+// run (measured on MI355X with a Zipf-skewed 256-expert routing: 3-6% faster
+// than interleaving the two kinds evenly or putting stream items first).
+// Each XCD gets a contiguous run of work ids per round (workgroups are dealt
+// to the 8 XCDs round robin), so consecutive m-tiles of one weight tile meet
+// in one L2 (7-15% faster than the plain order).
+constexpr int kMaxExperts = 1024;
+constexpr int kStreamTail = 32;
+
+template <class C, bool BF16>
+__global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ SA, int T,
+    const int32_t* __restrict__ RI, const int32_t* __restrict__ OFFS, int R, int E,
+    const uint8_t* __restrict__ W, const float* __restrict__ SW, int N, int K, void* __restrict__ Y) {
+  static_assert(C::NT == 256, "stream items use 4 waves");
+  static_assert(stream_part_bytes<2>() <= C::BUF, "stream partials fit in one stage");
+  FP8B_STAGES(C);
+  __shared__ int tstart[kMaxExperts + 1];  // first tile item of expert e
+  __shared__ int sstart[kMaxExperts + 1];  // first stream item of expert e
+  __shared__ int scan[2][C::NT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int tiles_n = N / C::BN, nkb = K / kBK, sblocks = N / kStreamRows;
+
+  auto off_at = [&](int e) { return min(max(OFFS[e], 0), R); };
+  auto rows_of = [&](int e) { return max(off_at(e + 1) - off_at(e), 0); };
+  auto tail_of = [&](int e) {  // rows handled by stream items
+    const int t = rows_of(e) % C::BM;
+    return t <= kStreamTail ? t : 0;
+  };
+  auto ntiles = [&](int e) { return ((rows_of(e) - tail_of(e) + C::BM - 1) / C::BM) * tiles_n; };
+  auto nstream = [&](int e) { return tail_of(e) > 0 ? sblocks : 0; };
+
+  // the two maps: block-wide inclusive scans of per-thread expert ranges
+  const int per = (E + C::NT - 1) / C::NT;
+  const int e0 = min(tid * per, E), e1 = min(e0 + per, E);
+  int lt = 0, ls = 0;
+  for (int e = e0; e < e1; ++e) {
+    lt += ntiles(e);
+    ls += nstream(e);
+  }
+  scan[0][tid] = lt;
+  scan[1][tid] = ls;
+  __syncthreads();
+  for (int o = 1; o < C::NT; o <<= 1) {
+    const int vt = tid >= o ? scan[0][tid - o] : 0;
+    const int vs = tid >= o ? scan[1][tid - o] : 0;
+    __syncthreads();
+    scan[0][tid] += vt;
+    scan[1][tid] += vs;
+    __syncthreads();
+  }
+  int rt = tid ? scan[0][tid - 1] : 0, rs = tid ? scan[1][tid - 1] : 0;
+  for (int e = e0; e < e1; ++e) {
+    tstart[e] = rt;
+    sstart[e] = rs;
+    rt += ntiles(e);
+    rs += nstream(e);
+  }
+  if (tid == C::NT - 1) {
+    tstart[E] = scan[0][C::NT - 1];
+    sstart[E] = scan[1][C::NT - 1];
+  }
+  __syncthreads();
+  const int n_tile = tstart[E], n_stream = sstart[E];
+  const int total = n_tile + n_stream;
+  // largest e with start[e] <= w
+  auto expert_of = [&](const int* start, int w) {
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (start[mid] <= w) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
+
+  const int G = gridDim.x;
+  const int slot = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  for (int base = 0; base < total; base += G) {
+    const int wk = base + slot;
+    if (wk >= total) break;
+    __syncthreads();  // the previous item may still read the stages / partials
+
+    if (wk < n_tile) {
+      const int e = expert_of(tstart, wk);
+      const int rb = off_at(e), re = rb + rows_of(e) - tail_of(e);
+      const int mt = (re - rb + C::BM - 1) / C::BM;
+      const int loc = wk - tstart[e];
+      const int tn = loc / mt, tm = loc - tn * mt;
+      const int r0 = rb + tm * C::BM, n0 = tn * C::BN;
+      auto token = [&](int r) { return min(max(RI[min(r0 + r, re - 1)], 0), T - 1); };
+
+      Src<C> src;
+      src.abase = A;
+      src.wbase = W + ((int64_t)e * N + n0) * K;
+      make_code_src<C>(src, [&](int r) { return (uint32_t)token(r) * (uint32_t)K; },
+                       [&](int r) { return (uint32_t)(r * K); });
+      src.scale_dst = -1;
+      src.sbase = reinterpret_cast<const uint8_t*>(SA);
+      src.soff = 0;
+      if (wave < C::NS_A) {
+        src.soff = (uint32_t)token(64 * wave + lane) * (uint32_t)(nkb * 4);
+        src.scale_dst = C::OFF_SA + 256 * wave;
+      } else if (wave == C::NS_A) {
+        src.sbase = reinterpret_cast<const uint8_t*>(SW + (int64_t)e * (N / 128) * nkb);
+        src.soff = (uint32_t)((n0 / 128 + min(lane, C::BN / 128 - 1)) * nkb * 4);
+        src.scale_dst = C::OFF_SB;
+      }
+      v4f acc[C::MI][C::NJ];
+      k_loop<C>(lds0, lds1, lds2, src, nkb, acc);
+      epilogue<C, BF16>(Y, acc, n0,
+                        [&](int r) -> int64_t { return r0 + r < re ? (int64_t)(r0 + r) * N : -1; });
+    } else {
+      const int sb = wk - n_tile;  // stream item index
+      const int e = expert_of(sstart, sb);
+      const int t = tail_of(e), r0 = off_at(e) + rows_of(e) - t;
+      const int n0 = (sb - sstart[e]) * kStreamRows;
+      const int l16 = lane & 15;
+      const uint8_t* wrow = W + ((int64_t)e * N + n0 + l16) * K;
+      const float* swrow = SW + ((int64_t)e * (N / 128) + n0 / 128) * nkb;
+      v4f* part = reinterpret_cast<v4f*>(lds0);
+      auto row_off = [&](int r) -> int64_t { return r < t ? (int64_t)(r0 + r) * N : -1; };
+      auto run = [&](auto mi) {
+        constexpr int MI = decltype(mi)::value;
+        const uint8_t* arow[MI];
+        const float* sarow[MI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const int tok = min(max(RI[r0 + min(16 * i + l16, t - 1)], 0), T - 1);
+          arow[i] = A + (int64_t)tok * K;
+          sarow[i] = SA + (int64_t)tok * nkb;
+        }
+        v4f acc[MI][kStreamNJ];
+        if (stream_rows<MI>(arow, sarow, wrow, K, swrow, nkb, part, acc))
+          stream_store<MI, BF16>(Y, acc, n0, row_off);
+      };
+      if (t <= 16)
+        run(std::integral_constant<int, 1>{});
+      else
+        run(std::integral_constant<int, 2>{});
+    }
+  }
 }
 
 // ---- host launchers ---------------------------------------------------------
@@ -753,6 +839,19 @@ static int cu_count() {
   return n;
 }
 
+template <int MI>
+static void launch_decode(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
+                          const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
+                          hipStream_t s) {
+  const dim3 grid((unsigned)(N / kStreamRows)), block(256);
+  if (out_bf16)
+    hipLaunchKernelGGL((decode_gemm_kernel<MI, true>), grid, block, 0, s, a, lda, sa, w, ldw, sw, (int)M, (int)N,
+                       (int)K, y, ldy);
+  else
+    hipLaunchKernelGGL((decode_gemm_kernel<MI, false>), grid, block, 0, s, a, lda, sa, w, ldw, sw, (int)M, (int)N,
+                       (int)K, y, ldy);
+}
+
 template <class C>
 static void launch_block(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
                          const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
@@ -770,6 +869,7 @@ static void launch_block(const uint8_t* a, int64_t lda, const float* sa, const u
 int launch_block_gemm(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
                       const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
                       hipStream_t s) {
+  // M <= 32: the streaming kernel (one or two 16-token subtiles)
   if (M <= 16)
     launch_decode<1>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
   else if (M <= 32)
@@ -803,7 +903,7 @@ int launch_grouped_gemm(const uint8_t* a, const float* sa, int64_t T, const int3
   using C = GroupedCfg;
   // enough persistent workgroups to fill every CU (at its occupancy), never
   // more than the largest possible number of tiles
-  const int64_t max_tiles = ((R + C::BM - 1) / C::BM + E) * (N / C::BN);
+  const int64_t max_tiles = ((R + C::BM - 1) / C::BM + E) * (N / C::BN) + E * (N / kStreamRows);
   const int64_t nwg = std::max<int64_t>(1, std::min<int64_t>((512 / C::NT) * (int64_t)cu_count(), max_tiles));
   const dim3 grid((unsigned)nwg), block(C::NT);
   if (out_bf16)

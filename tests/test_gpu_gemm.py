@@ -202,6 +202,39 @@ def test_grouped_skewed_with_empty_experts(F, orc):
     assert_parity(yg, yr, bnd, True, "moe skewed")
 
 
+def _moe_counts_case(counts, T, N, K, seed):
+    """A routing with the given rows per expert (tokens drawn at random)."""
+    counts = np.asarray(counts, np.int64)
+    g = W.gen(seed)
+    x = W.activations(T, K, max(1, round(0.005 * K)), 50.0, g)
+    w = torch.stack([W.weights(N, K, 0.02, g) for _ in counts])
+    offs = np.zeros(len(counts) + 1, np.int64)
+    offs[1:] = np.cumsum(counts)
+    ri = np.random.default_rng(seed).integers(0, T, size=int(offs[-1]))
+    experts = np.repeat(np.arange(len(counts)), counts)
+    return W.MoeCase(x, w, torch.from_numpy(ri.astype(np.int32)), torch.from_numpy(offs.astype(np.int32)),
+                     torch.from_numpy(experts.astype(np.int32)))
+
+
+def test_grouped_every_tail_kind(F, orc):
+    """Expert sizes around every branch of the work map: empty experts,
+    short tails on the streaming path (1, 16 / 17, 32 rows: one and two
+    16-row subtiles), longer tails padded into a 128-row tile (33, 127),
+    whole tiles (128, 256) and whole tiles plus either kind of tail."""
+    counts = [0, 1, 16, 17, 32, 33, 127, 128, 129, 144, 160, 161, 256, 300, 0, 5]
+    case = _moe_counts_case(counts, T=200, N=256, K=640, seed=41)
+    yg, yr, bnd = _moe_run(F, orc, case)
+    assert_parity(yg, yr, bnd, True, "moe tails")
+
+
+def test_grouped_only_short_experts(F, orc):
+    """Every expert below 32 rows: no tile items at all."""
+    counts = [3, 0, 31, 7, 1, 0, 20, 16]
+    case = _moe_counts_case(counts, T=64, N=384, K=1152, seed=43)
+    yg, yr, bnd = _moe_run(F, orc, case)
+    assert_parity(yg, yr, bnd, True, "moe short")
+
+
 def test_grouped_full_sampled(F, orc):
     case = W.moe_case(device=DEV)
     offs = case.offs.numpy()
