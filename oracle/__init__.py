@@ -59,6 +59,9 @@ def lib():
         L.orc_scale_pow2_exp.argtypes = [ctypes.c_float]
         L.orc_act_quant.argtypes = [_c_u16p, _i64, _i64, _i64, ctypes.c_int,
                                     ctypes.c_int, _c_u8p, _i64, ctypes.c_void_p]
+        L.orc_dequant_one.restype = ctypes.c_uint16
+        L.orc_dequant_one.argtypes = [ctypes.c_uint8, ctypes.c_float]
+        L.orc_weight_dequant.argtypes = [_c_u8p, _i64, _i64, _i64, _c_f32p, _c_u16p, _i64]
         L.orc_weight_quant.argtypes = [_c_u16p, _i64, _i64, _i64, ctypes.c_int,
                                        _c_u8p, _i64, _c_f32p]
         L.orc_block_gemm.argtypes = [_c_u8p, _i64, _c_f32p, _c_u8p, _i64, _c_f32p,
@@ -151,6 +154,22 @@ def weight_quant(w_bits, scale_fmt: int):
     if rc != 0:
         raise ValueError("orc_weight_quant rejected its arguments")
     return q, s
+
+
+def weight_dequant(q, scales):
+    """codes uint8 [N, K] + fp32 scales [N/128, K/128] -> bf16 bits uint16 [N, K]."""
+    q = _c(q, np.uint8)
+    s = _c(scales, np.float32)
+    N, K = q.shape
+    w = np.empty((N, K), np.uint16)
+    rc = lib().orc_weight_dequant(_p(q, _c_u8p), N, K, K, _p(s, _c_f32p), _p(w, _c_u16p), K)
+    if rc != 0:
+        raise ValueError("orc_weight_dequant rejected its arguments")
+    return w
+
+
+def dequant_one(code: int, d: float) -> int:
+    return int(lib().orc_dequant_one(int(code), float(d)))
 
 
 # ---- GEMM references -----------------------------------------------------

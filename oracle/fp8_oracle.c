@@ -234,6 +234,63 @@ int orc_weight_quant(const uint16_t *w, int64_t N, int64_t K, int64_t ldw,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Weight dequantisation.  [P4] dispatch snippet, bf16 branch:              */
+/* weight_dequant(weight, weight.scale) turns the FP8 weights with their    */
+/* 128x128 block scales back into bf16 (the fp8_cast_bf16 conversion);     */
+/* [P5] "FP8 也需要 scale": x_hat = s * x_fp8.  Reading: the product of a   */
+/* code's value and its block scale is formed in fp32 (the scales' type),   */
+/* i.e. rounded once to fp32, and that fp32 value is rounded to bf16,       */
+/* nearest even.                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Round a finite double that is exactly an fp32 value to bf16 (8
+   significant bits, fp32's exponent range, subnormals down to 2^-133),
+   nearest, ties to even; overflow gives +-Inf.  Returns the bf16 bits. */
+static uint16_t round_f32_to_bf16(float f) {
+  union { float f; uint32_t u; } cv;
+  double v = (double)f, q, r;
+  int e;
+  if (isnan(f)) {
+    cv.f = f;
+    return (uint16_t)((cv.u >> 16) | 0x40u);
+  }
+  if (v == 0.0 || isinf(v)) {
+    cv.f = f;
+    return (uint16_t)(cv.u >> 16);
+  }
+  frexp(fabs(v), &e);                     /* |v| in [2^(e-1), 2^e)          */
+  if (e - 1 < -126) e = -125;             /* subnormal range: fixed quantum */
+  q = ldexp(1.0, e - 1 - 7);              /* bf16 spacing at this binade    */
+  r = nearbyint(v / q) * q;               /* exact: v/q and r*q are exact   */
+  if (fabs(r) >= ldexp(1.0, 128)) r = copysign(INFINITY, v);
+  cv.f = (float)r;                        /* r is a bf16 value: exact       */
+  if (r == 0.0) cv.f = (float)copysign(0.0, v);
+  return (uint16_t)(cv.u >> 16);
+}
+
+uint16_t orc_dequant_one(uint8_t code, float d) {
+  double v = orc_e4m3_value(code);
+  float p;
+  if (isnan(v)) return 0x7FC0u;
+  p = (float)(v * (double)d);  /* exact product (<= 28 bits), one rounding */
+  return round_f32_to_bf16(p);
+}
+
+int orc_weight_dequant(const uint8_t *q, int64_t N, int64_t K, int64_t ldq,
+                       const float *scales, uint16_t *w, int64_t ldw) {
+  int64_t n;
+  if (!q || !scales || !w || N < 0 || K < 0) return -1;
+  if (N % 128 != 0 || K % 128 != 0 || ldq < K || ldw < K) return -1;
+#pragma omp parallel for schedule(static)
+  for (n = 0; n < N; ++n) {
+    int64_t k;
+    for (k = 0; k < K; ++k)
+      w[n * ldw + k] = orc_dequant_one(q[n * ldq + k], scales[(n / 128) * (K / 128) + k / 128]);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* GEMM references.  [P2] section 3: FP8 x FP8 products accumulated in FP32 */
 /* with per-block scales; [P4]: fp8_gemm(x, scale, weight, weight.scale).   */
 /* Here the inner products are exact: 512 * val(code) is an integer for    */

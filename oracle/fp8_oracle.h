@@ -36,6 +36,8 @@
  *    amax <= 448 * 2^e, clamped to [-127, 127].
  *  - amax == 0: d = 1 (e = 0).
  *  - A negative value that rounds to zero keeps its sign (code 0x80).
+ *  - Weight dequantisation forms value(code) * scale in fp32 and rounds that
+ *    to bf16 (nearest even): two roundings, as the scales are fp32.
  *
  * All functions are reentrant; buffers are owned by the caller.
  */
@@ -80,6 +82,14 @@ int orc_act_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
  * scales fp32 [N/128][K/128]. scale_fmt is ORC_SCALE_FP32 or _UE8M0. */
 int orc_weight_quant(const uint16_t *w, int64_t N, int64_t K, int64_t ldw,
                      int scale_fmt, uint8_t *q, int64_t ldq, float *scales);
+
+/* ---- weight dequantisation ([P4] weight_dequant; [P5] x_hat = s * x_fp8) --
+ * w[n][k] = bf16_RNE(fp32(value(q[n][k]) * scales[n/128][k/128])): the
+ * product is rounded once to fp32, then to bf16.  NaN codes give 0x7FC0.
+ * N, K multiples of 128.  Returns 0, or -1 on bad arguments. */
+uint16_t orc_dequant_one(uint8_t code, float d);
+int orc_weight_dequant(const uint8_t *q, int64_t N, int64_t K, int64_t ldq,
+                       const float *scales, uint16_t *w, int64_t ldw);
 
 /* ---- block-scaled GEMM reference: y[m][n] = sum_kb sa[m][kb] *
  * sw[n/128][kb] * sum_{k in kb} val(a[m][k]) * val(w[n][k]).
