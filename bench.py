@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--no-legs", action="store_true", help="time the headline step only")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
-    p.add_argument("--only", default="", help="run one leg only: decode|mx|moe|prefill")
+    p.add_argument("--only", default="", help="run one leg only: decode|mx|moe|dequant")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (a kernel of known traffic, for "
                         "scaling profiler byte counters)")
@@ -283,6 +283,18 @@ def run_legs(torch, F, W, dev, only=""):
                        "GBps": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
                        "active_experts": active, "max_rows": int(counts.max())}
         del wq, ws, a, sa, y
+        torch.cuda.empty_cache()
+    if only in ("", "dequant"):
+        c = W.prefill_linear(device=dev)
+        N, K = c.w.shape
+        wq, ws = F.fp8_weight_quant(c.w, "fp32")
+        del c
+        out = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+        t = timed(torch, lambda: F.fp8_weight_dequant(wq, ws, w=out), iters)
+        nbytes = N * K * 3 + (N // 128) * (K // 128) * 4
+        legs["weight_dequant"] = {"shape": [N, K], "us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+                                  "hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)}
+        del wq, ws, out
         torch.cuda.empty_cache()
     return legs
 

@@ -62,6 +62,8 @@ def lib():
         L.mxfp8_gemm.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, i64, vp, i64, vp]
         L.fp8_grouped_gemm.restype = ci
         L.fp8_grouped_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp, i64, i64, vp, ci, vp]
+        L.fp8_weight_dequant.restype = ci
+        L.fp8_weight_dequant.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp]
         L.fp8_cast_f32.restype = ci
         L.fp8_cast_f32.argtypes = [vp, i64, ci, vp, vp]
         _lib = L
@@ -132,6 +134,20 @@ def fp8_weight_quant(w: torch.Tensor, scale_fmt="fp32", q=None, scales=None):
                                 _p(scales), _stream(w))
     _check("fp8_weight_quant", rc)
     return q, scales
+
+
+def fp8_weight_dequant(q: torch.Tensor, scales: torch.Tensor, w=None):
+    """FP8 weights with 128x128 block scales back to bf16:
+    w[n, k] = bf16(fp32(value(q[n, k]) * scales[n/128, k/128]))."""
+    _need(q.dtype == torch.uint8 and q.dim() == 2 and q.stride(1) == 1, "q must be 2-D uint8, rows contiguous")
+    _need(scales.dtype == torch.float32 and scales.is_contiguous(), "scales must be contiguous float32")
+    N, K = q.shape
+    if w is None:
+        w = torch.empty(N, K, dtype=torch.bfloat16, device=q.device)
+    _need(w.dtype == torch.bfloat16 and w.stride(1) == 1, "w must be bf16, rows contiguous")
+    rc = lib().fp8_weight_dequant(_p(q), N, K, q.stride(0), _p(scales), _p(w), w.stride(0), _stream(q))
+    _check("fp8_weight_dequant", rc)
+    return w
 
 
 def fp8_block_gemm(a, a_scales, w, w_scales, out_dtype=torch.bfloat16, y=None):

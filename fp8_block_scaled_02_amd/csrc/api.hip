@@ -100,6 +100,17 @@ FP8B_EXPORT int fp8_grouped_gemm(const uint8_t* a, const float* a_scales, int64_
                                      out_dtype == FP8B_OUT_BF16, as_stream(stream));
 }
 
+FP8B_EXPORT int fp8_weight_dequant(const uint8_t* q, int64_t N, int64_t K, int64_t ld_q, const float* scales, void* w,
+                                   int64_t ld_w, void* stream) {
+  if (!q || !scales || !w) return FP8B_EINVAL;
+  if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim || N % 128 != 0 || K % 128 != 0) return FP8B_EINVAL;
+  if (ld_q < K || ld_w < K) return FP8B_EINVAL;
+  if (!aligned(q, 16) || ld_q % 16 != 0 || !aligned(w, 16) || ld_w % 8 != 0 || !aligned(scales, 4))
+    return FP8B_EALIGN;
+  if (N * (K / 16) / 256 >= INT32_MAX) return FP8B_EINVAL;
+  return fp8blk::launch_weight_dequant(q, N, K, ld_q, scales, w, ld_w, as_stream(stream));
+}
+
 FP8B_EXPORT int fp8_cast_f32(const float* x, int64_t n, int fmt, uint8_t* q, void* stream) {
   if (fmt != FP8B_FMT_E4M3 && fmt != FP8B_FMT_E5M2) return FP8B_EUNSUPPORTED;
   if (!x || !q || n < 0) return FP8B_EINVAL;

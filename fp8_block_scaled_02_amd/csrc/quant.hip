@@ -173,6 +173,36 @@ __global__ __launch_bounds__(256) void cast_kernel(const float* __restrict__ x, 
     if (i + j < n) q[i + j] = (uint8_t)(p >> (8 * j));
 }
 
+// Weight dequantisation (the bf16 branch of the DeepSeek-V3 guide's
+// dispatch snippet, weight_dequant(weight, weight.scale); x_hat = s * x_fp8
+// of "量化: FP8 与混合精度推理", section "FP8 也需要 scale"):
+//   w = bf16_RNE(fp32(value(code) * d)), d the code's 128x128 block scale.
+// E4M3 -> fp32 is exact; the fp32 multiply is the one rounding of the
+// product.  HBM-bound: each thread reads 16 codes (one 16-byte load) and
+// writes 16 bf16 (two 16-byte stores).
+__global__ __launch_bounds__(256) void weight_dequant_kernel(
+    const uint8_t* __restrict__ q, int64_t N, int64_t K, int64_t ldq, const float* __restrict__ scales,
+    uint16_t* __restrict__ w, int64_t ldw) {
+  const int64_t cpr = K / 16;  // 16-code chunks per row
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= N * cpr) return;
+  const int64_t n = c / cpr, k = (c - n * cpr) * 16;
+  const float d = scales[(n / 128) * (K / 128) + k / 128];
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q + n * ldq + k));
+  uint32_t out[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)v[i], 1.0f, false);  // bytes 0, 1
+    const f2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)v[i], 1.0f, true);   // bytes 2, 3
+    out[2 * i] = f32_to_bf16_bits(lo[0] * d) | (f32_to_bf16_bits(lo[1] * d) << 16);
+    out[2 * i + 1] = f32_to_bf16_bits(hi[0] * d) | (f32_to_bf16_bits(hi[1] * d) << 16);
+  }
+  uint4* dst = reinterpret_cast<uint4*>(w + n * ldw + k);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+}
+
 // ---- host launchers --------------------------------------------------------
 constexpr int kActUnroll = 4;
 
@@ -205,6 +235,14 @@ int launch_weight_quant(const void* w, int64_t N, int64_t K, int64_t ldw, int fm
     hipLaunchKernelGGL(weight_quant_kernel<0>, grid, dim3(256), 0, s, wp, N, K, ldw, q, ldq, scales);
   else
     hipLaunchKernelGGL(weight_quant_kernel<1>, grid, dim3(256), 0, s, wp, N, K, ldw, q, ldq, scales);
+  return check_launch();
+}
+
+int launch_weight_dequant(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, const float* scales,
+                          void* w, int64_t ldw, hipStream_t s) {
+  const dim3 grid((unsigned)((N * (K / 16) + 255) / 256));
+  hipLaunchKernelGGL(weight_dequant_kernel, grid, dim3(256), 0, s, q, N, K, ldq, scales,
+                     static_cast<uint16_t*>(w), ldw);
   return check_launch();
 }
 

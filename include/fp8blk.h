@@ -190,6 +190,26 @@ int fp8_grouped_gemm(const uint8_t *a, const float *a_scales, int64_t T,
                      int out_dtype, void *stream);
 
 /*
+ * fp8_weight_dequant -- weight dequantisation, the bf16 branch of the
+ * DeepSeek-V3 guide's dispatch snippet (weight_dequant(weight,
+ * weight.scale), used to turn the FP8 checkpoint into bf16) and
+ * x_hat = s * x_fp8 of "量化: FP8 与混合精度推理", section "FP8 也需要 scale":
+ *
+ *   w[n][k] = bf16_RNE(fp32(value(q[n][k]) * scales[n/128][k/128]))
+ *   (the product is rounded once to fp32, then to bf16, nearest even).
+ *
+ *   q       codes [N][ld_q], 16-byte aligned, ld_q % 16 == 0, ld_q >= K.
+ *   N, K    > 0, multiples of 128.
+ *   scales  float [N/128][K/128], contiguous (fp8_weight_quant's layout).
+ *   w       bf16 [N][ld_w], 16-byte aligned, ld_w % 8 == 0, ld_w >= K.
+ *   NaN codes (0x7F, 0xFF) give NaN; products beyond bf16's range give
+ *   +-Inf.
+ */
+int fp8_weight_dequant(const uint8_t *q, int64_t N, int64_t K, int64_t ld_q,
+                       const float *scales, void *w, int64_t ld_w,
+                       void *stream);
+
+/*
  * fp8_cast_f32 -- FP8Cast of "量化: FP8 与混合精度推理" (x_fp8 =
  * FP8Cast(x / s)) with s = 1: clamp each fp32 value to +-Fmax (448 for
  * E4M3, 57344 for E5M2) and round to nearest, ties to even.

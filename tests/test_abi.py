@@ -26,7 +26,7 @@ def L():
 def test_header_declares_the_boundary():
     assert _declared() == sorted([
         "fp8b_abi_version", "fp8b_status_string", "fp8_act_quant", "fp8_weight_quant",
-        "fp8_block_gemm", "mxfp8_gemm", "fp8_grouped_gemm", "fp8_cast_f32"])
+        "fp8_block_gemm", "mxfp8_gemm", "fp8_grouped_gemm", "fp8_weight_dequant", "fp8_cast_f32"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -71,6 +71,16 @@ def test_weight_quant_validation(L):
     assert f(GOOD, 200, 256, 256, 0, GOOD, 256, GOOD, NULL) == -1
     assert f(GOOD, 256, 256, 256, 0, NULL, 256, GOOD, NULL) == -1
     assert f(ODD, 256, 256, 256, 0, GOOD, 256, GOOD, NULL) == -2
+
+
+def test_weight_dequant_validation(L):
+    f = L.fp8_weight_dequant
+    assert f(NULL, 256, 256, 256, GOOD, GOOD, 256, NULL) == -1
+    assert f(GOOD, 200, 256, 256, GOOD, GOOD, 256, NULL) == -1           # N % 128
+    assert f(GOOD, 256, 256, 128, GOOD, GOOD, 256, NULL) == -1           # ld_q < K
+    assert f(ODD, 256, 256, 256, GOOD, GOOD, 256, NULL) == -2
+    assert f(GOOD, 256, 256, 264, GOOD, GOOD, 256, NULL) == -2           # ld_q % 16
+    assert f(GOOD, 256, 256, 256, GOOD, GOOD, 260, NULL) == -2           # ld_w % 8
 
 
 def test_block_gemm_validation(L):

@@ -195,3 +195,48 @@ def test_act_quant_fp32_scales_every_block_magnitude(F, orc, block):
     x = torch.from_numpy(vals[: (nb // 4) * 4].reshape(-1, 4 * block)).to(torch.bfloat16)
     assert float(x.abs().max()) <= 3.39e38
     _assert_same(*_run_act(F, orc, x, block, "fp32"), f"every amax block {block}")
+
+
+# ---- weight dequantisation ---------------------------------------------------
+def _deq_check(gpu_bits, want, what):
+    g = gpu_bits.astype(np.uint16)
+    nan_w = ((want & 0x7F80) == 0x7F80) & ((want & 0x7F) != 0)
+    nan_g = ((g & 0x7F80) == 0x7F80) & ((g & 0x7F) != 0)
+    assert (nan_w == nan_g).all(), f"{what}: NaN positions differ"
+    bad = np.argwhere((g != want) & ~nan_w)
+    assert len(bad) == 0, f"{what}: {len(bad)} mismatches, first at {tuple(bad[0])}: gpu {g[tuple(bad[0])]:#06x} oracle {want[tuple(bad[0])]:#06x}"
+
+
+def test_weight_dequant_every_code_wide_scales(F, orc):
+    """Every code (NaN codes included) against fp32 block scales spread over
+    the whole fp32 range, in both signs of magnitude overflow/underflow."""
+    rng = np.random.default_rng(31)
+    q = rng.integers(0, 256, size=(512, 1024), dtype=np.uint8)
+    q[0, :256] = np.arange(256, dtype=np.uint8)
+    s = np.exp(rng.uniform(-87, 87, size=(4, 8))).astype(np.float32)   # finite fp32
+    s[0, 0], s[1, 1], s[2, 2], s[3, 3] = 1.0, 2.0 ** -140, 3.0e38, 1.0 / 448
+    w = F.fp8_weight_dequant(torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV))
+    torch.cuda.synchronize()
+    _deq_check(_np(w.view(torch.int16)).view(np.uint16), orc.weight_dequant(q, s), "wide scales")
+
+
+def test_weight_dequant_strided(F, orc):
+    g = W.gen(6)
+    wq, ws = F.fp8_weight_quant(W.weights(256, 384, 0.02, g).to(DEV), "fp32")
+    qbig = torch.zeros(256, 400, dtype=torch.uint8, device=DEV)
+    qbig[:, :384] = wq
+    out = torch.full((256, 392), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    F.fp8_weight_dequant(qbig[:, :384], ws, w=out[:, :384])
+    torch.cuda.synchronize()
+    o = _np(out.view(torch.int16)).view(np.uint16)
+    assert (o[:, 384:] == 0xFFFF).all()
+    _deq_check(o[:, :384], orc.weight_dequant(_np(wq), _np(ws)), "strided")
+
+
+@pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
+def test_weight_dequant_prefill_full(F, orc, fmt):
+    c = W.prefill_linear(device=DEV)
+    wq, ws = F.fp8_weight_quant(c.w, fmt)
+    w = F.fp8_weight_dequant(wq, ws)
+    torch.cuda.synchronize()
+    _deq_check(_np(w.view(torch.int16)).view(np.uint16), orc.weight_dequant(_np(wq), _np(ws)), f"18432x7168 {fmt}")
