@@ -62,6 +62,8 @@ def lib():
         L.orc_dequant_one.restype = ctypes.c_uint16
         L.orc_dequant_one.argtypes = [ctypes.c_uint8, ctypes.c_float]
         L.orc_weight_dequant.argtypes = [_c_u8p, _i64, _i64, _i64, _c_f32p, _c_u16p, _i64]
+        L.orc_kv_quant.argtypes = [_c_u16p, _i64, _i64, _i64, _c_u8p, _i64, _c_f32p]
+        L.orc_kv_dequant.argtypes = [_c_u8p, _i64, _i64, _i64, _c_f32p, _c_u16p, _i64]
         L.orc_weight_quant.argtypes = [_c_u16p, _i64, _i64, _i64, ctypes.c_int,
                                        _c_u8p, _i64, _c_f32p]
         L.orc_block_gemm.argtypes = [_c_u8p, _i64, _c_f32p, _c_u8p, _i64, _c_f32p,
@@ -170,6 +172,28 @@ def weight_dequant(q, scales):
 
 def dequant_one(code: int, d: float) -> int:
     return int(lib().orc_dequant_one(int(code), float(d)))
+
+
+def kv_quant(x_bits):
+    """x_bits: uint16 (bf16) [T, D] -> (E5M2 codes uint8 [T, D], fp32 scales [T])."""
+    x = _c(x_bits, np.uint16)
+    T, D = x.shape
+    q = np.empty((T, D), np.uint8)
+    s = np.empty(T, np.float32)
+    if lib().orc_kv_quant(_p(x, _c_u16p), T, D, D, _p(q, _c_u8p), D, _p(s, _c_f32p)) != 0:
+        raise ValueError("orc_kv_quant rejected its arguments")
+    return q, s
+
+
+def kv_dequant(q, scales):
+    """E5M2 codes [T, D] + fp32 scales [T] -> bf16 bits uint16 [T, D]."""
+    q = _c(q, np.uint8)
+    s = _c(scales, np.float32)
+    T, D = q.shape
+    out = np.empty((T, D), np.uint16)
+    if lib().orc_kv_dequant(_p(q, _c_u8p), T, D, D, _p(s, _c_f32p), _p(out, _c_u16p), D) != 0:
+        raise ValueError("orc_kv_dequant rejected its arguments")
+    return out
 
 
 # ---- GEMM references -----------------------------------------------------

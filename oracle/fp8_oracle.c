@@ -291,6 +291,55 @@ int orc_weight_dequant(const uint8_t *q, int64_t N, int64_t K, int64_t ldq,
 }
 
 /* ------------------------------------------------------------------------ */
+/* KV-cache quantisation.  [P2] section 4 (KV cache): E5M2 rather than     */
+/* E4M3 for its range (largest finite 57344), with one scale per token     */
+/* taken from the token's real-time amax ([P2]'s precision table row "KV   */
+/* cache | E5M2 | per-token").  Reading: one row of the cache (a token's   */
+/* K or V) is one block: d = fp32(amax / 57344) (d = 1 for amax = 0),      */
+/* q = E5M2(clamp(fp32(x / d), +-57344)); dequantisation is                */
+/* bf16_RNE(fp32(value(q) * d)).                                            */
+/* ------------------------------------------------------------------------ */
+int orc_kv_quant(const uint16_t *x, int64_t T, int64_t D, int64_t ldx, uint8_t *q,
+                 int64_t ldq, float *scales) {
+  int64_t t;
+  if (!x || !q || !scales || T < 0 || D <= 0 || ldx < D || ldq < D) return -1;
+#pragma omp parallel for schedule(static)
+  for (t = 0; t < T; ++t) {
+    int64_t k;
+    float amax = 0.0f, d;
+    for (k = 0; k < D; ++k) {
+      float a = fabsf(bf16_to_f32(x[t * ldx + k]));
+      if (a > amax) amax = a;
+    }
+    d = (amax == 0.0f) ? 1.0f : amax / 57344.0f;  /* one IEEE division */
+    for (k = 0; k < D; ++k) {
+      float v = bf16_to_f32(x[t * ldx + k]) / d;  /* fp32 quotient      */
+      if (v > 57344.0f) v = 57344.0f;
+      if (v < -57344.0f) v = -57344.0f;
+      q[t * ldq + k] = orc_e5m2_encode(v);
+    }
+    scales[t] = d;
+  }
+  return 0;
+}
+
+int orc_kv_dequant(const uint8_t *q, int64_t T, int64_t D, int64_t ldq, const float *scales,
+                   uint16_t *out, int64_t ldo) {
+  int64_t t;
+  if (!q || !scales || !out || T < 0 || D <= 0 || ldq < D || ldo < D) return -1;
+#pragma omp parallel for schedule(static)
+  for (t = 0; t < T; ++t) {
+    int64_t k;
+    for (k = 0; k < D; ++k) {
+      double v = orc_e5m2_value(q[t * ldq + k]);
+      out[t * ldo + k] = isnan(v) ? (uint16_t)0x7FC0u
+                                  : round_f32_to_bf16((float)(v * (double)scales[t]));
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* GEMM references.  [P2] section 3: FP8 x FP8 products accumulated in FP32 */
 /* with per-block scales; [P4]: fp8_gemm(x, scale, weight, weight.scale).   */
 /* Here the inner products are exact: 512 * val(code) is an integer for    */

@@ -15,7 +15,8 @@
  *       (order of operations: divide by the scale, clamp to +-448, cast).
  *  [P2] "LLM 推理的 FP8 混合精度工程 2026" (blog.lonae.com), section 2
  *       (quantizer Q(x) = clamp(round(x*s), -Fmax, Fmax) * s^-1, Fmax 448 /
- *       57344) and section 3 (FP32 accumulation, 128x128 blockwise scales).
+ *       57344), section 3 (FP32 accumulation, 128x128 blockwise scales) and
+ *       section 4 (KV cache in E5M2 with per-token scales).
  *  [P3] "FP8 推理" study notes (luoboask.github.io), the format tables and
  *       the "Dynamic Scaling" section (scale = max|tensor| / 448,
  *       FP8 value = FP32 value / scale).
@@ -38,6 +39,8 @@
  *  - A negative value that rounds to zero keeps its sign (code 0x80).
  *  - Weight dequantisation forms value(code) * scale in fp32 and rounds that
  *    to bf16 (nearest even): two roundings, as the scales are fp32.
+ *  - KV cache: one E5M2 scale per cache row (a token's K or V), from the
+ *    row's amax; percentile clipping is a calibration policy, not modelled.
  *
  * All functions are reentrant; buffers are owned by the caller.
  */
@@ -90,6 +93,16 @@ int orc_weight_quant(const uint16_t *w, int64_t N, int64_t K, int64_t ldw,
 uint16_t orc_dequant_one(uint8_t code, float d);
 int orc_weight_dequant(const uint8_t *q, int64_t N, int64_t K, int64_t ldq,
                        const float *scales, uint16_t *w, int64_t ldw);
+
+/* ---- KV cache ([P2] section 4: E5M2, one scale per token) ----------------
+ * Per row t of x [T][D]: amax over the row, d = fp32(amax / 57344) (1 if
+ * amax = 0), q = E5M2(clamp(fp32(x / d), +-57344)), scales[t] = d.
+ * Dequantisation: out = bf16_RNE(fp32(value(q) * d)); NaN codes give
+ * 0x7FC0, Inf codes give +-Inf.  Return 0, or -1 on bad arguments. */
+int orc_kv_quant(const uint16_t *x, int64_t T, int64_t D, int64_t ldx, uint8_t *q,
+                 int64_t ldq, float *scales);
+int orc_kv_dequant(const uint8_t *q, int64_t T, int64_t D, int64_t ldq, const float *scales,
+                   uint16_t *out, int64_t ldo);
 
 /* ---- block-scaled GEMM reference: y[m][n] = sum_kb sa[m][kb] *
  * sw[n/128][kb] * sum_{k in kb} val(a[m][k]) * val(w[n][k]).

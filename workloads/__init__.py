@@ -38,6 +38,8 @@ CONFIGS = {
     "prefill": dict(M=4096, K=7168, N=18432),
     "mx": dict(M=8192, K=8192, N=8192),
     "moe": dict(T=4096, E=256, topk=8, N=2048, K=7168),
+    # KV cache of a 32K-token context: 8 KV heads x 128 per token, K or V
+    "kv": dict(T=32768, D=1024),
 }
 
 
@@ -84,6 +86,15 @@ def mx_operand(R: int, K: int, g: torch.Generator, block: int = 32,
     u = lo + (hi - lo) * u
     z = z.view(R, K // block, block) * torch.exp2(u).unsqueeze(-1)
     return z.view(R, K).to(torch.bfloat16)
+
+
+def kv_rows(T: int, D: int, g: torch.Generator, lo: float = -8.0, hi: float = 8.0) -> torch.Tensor:
+    """K or V cache rows: bf16(z * 2^u), z ~ N(0,1), u ~ U(lo, hi) per token,
+    so token magnitudes differ by orders of magnitude along the sequence."""
+    dev = g.device
+    z = torch.randn(T, D, generator=g, device=dev, dtype=torch.float32)
+    u = lo + (hi - lo) * torch.rand(T, 1, generator=g, device=dev, dtype=torch.float32)
+    return (z * torch.exp2(u)).to(torch.bfloat16)
 
 
 def routing(T: int, E: int, topk: int, s: float, g: torch.Generator):
