@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--no-legs", action="store_true", help="time the headline step only")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
-    p.add_argument("--only", default="", help="run one leg only: decode|mx|moe|dequant")
+    p.add_argument("--only", default="", help="run one leg only: decode|mx|moe|dequant|kv")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (a kernel of known traffic, for "
                         "scaling profiler byte counters)")
@@ -295,6 +295,19 @@ def run_legs(torch, F, W, dev, only=""):
         legs["weight_dequant"] = {"shape": [N, K], "us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
                                   "hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)}
         del wq, ws, out
+        torch.cuda.empty_cache()
+    if only in ("", "kv"):
+        c = W.CONFIGS["kv"]
+        T, D = c["T"], c["D"]
+        x = W.kv_rows(T, D, W.gen(12, dev))
+        q, sc = F.fp8_kv_quant(x)
+        out = torch.empty(T, D, dtype=torch.bfloat16, device=dev)
+        t_q = timed(torch, lambda: F.fp8_kv_quant(x, q=q, scales=sc), iters)
+        t_d = timed(torch, lambda: F.fp8_kv_dequant(q, sc, out=out), iters)
+        nbytes = T * D * 3 + T * 4
+        legs["kv_cache"] = {"shape": [T, D], "quant_us": round(t_q * 1e6, 2), "quant_GBps": round(nbytes / t_q / 1e9, 1),
+                            "dequant_us": round(t_d * 1e6, 2), "dequant_GBps": round(nbytes / t_d / 1e9, 1)}
+        del x, q, sc, out
         torch.cuda.empty_cache()
     return legs
 

@@ -64,6 +64,10 @@ def lib():
         L.fp8_grouped_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp, i64, i64, vp, ci, vp]
         L.fp8_weight_dequant.restype = ci
         L.fp8_weight_dequant.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp]
+        L.fp8_kv_quant.restype = ci
+        L.fp8_kv_quant.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
+        L.fp8_kv_dequant.restype = ci
+        L.fp8_kv_dequant.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp]
         L.fp8_cast_f32.restype = ci
         L.fp8_cast_f32.argtypes = [vp, i64, ci, vp, vp]
         _lib = L
@@ -148,6 +152,32 @@ def fp8_weight_dequant(q: torch.Tensor, scales: torch.Tensor, w=None):
     rc = lib().fp8_weight_dequant(_p(q), N, K, q.stride(0), _p(scales), _p(w), w.stride(0), _stream(q))
     _check("fp8_weight_dequant", rc)
     return w
+
+
+def fp8_kv_quant(x: torch.Tensor, q=None, scales=None):
+    """KV-cache rows x bf16 [T, D] -> (E5M2 codes uint8 [T, D], fp32 scales [T]),
+    one scale per row (d = amax / 57344)."""
+    _need(x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1, "x must be 2-D bf16, rows contiguous")
+    T, D = x.shape
+    if q is None:
+        q = torch.empty(T, D, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(T, dtype=torch.float32, device=x.device)
+    rc = lib().fp8_kv_quant(_p(x), T, D, x.stride(0), _p(q), q.stride(0), _p(scales), _stream(x))
+    _check("fp8_kv_quant", rc)
+    return q, scales
+
+
+def fp8_kv_dequant(q: torch.Tensor, scales: torch.Tensor, out=None):
+    """E5M2 codes [T, D] + fp32 row scales [T] -> bf16 [T, D]."""
+    _need(q.dtype == torch.uint8 and q.dim() == 2 and q.stride(1) == 1, "q must be 2-D uint8, rows contiguous")
+    _need(scales.dtype == torch.float32 and scales.is_contiguous(), "scales must be contiguous float32")
+    T, D = q.shape
+    if out is None:
+        out = torch.empty(T, D, dtype=torch.bfloat16, device=q.device)
+    rc = lib().fp8_kv_dequant(_p(q), T, D, q.stride(0), _p(scales), _p(out), out.stride(0), _stream(q))
+    _check("fp8_kv_dequant", rc)
+    return out
 
 
 def fp8_block_gemm(a, a_scales, w, w_scales, out_dtype=torch.bfloat16, y=None):

@@ -111,6 +111,26 @@ FP8B_EXPORT int fp8_weight_dequant(const uint8_t* q, int64_t N, int64_t K, int64
   return fp8blk::launch_weight_dequant(q, N, K, ld_q, scales, w, ld_w, as_stream(stream));
 }
 
+FP8B_EXPORT int fp8_kv_quant(const void* x, int64_t T, int64_t D, int64_t ld_x, uint8_t* q, int64_t ld_q, float* scales,
+                             void* stream) {
+  if (!x || !q || !scales) return FP8B_EINVAL;
+  if (T < 0 || T > kMaxDim || D <= 0 || D > 16384 || D % 16 != 0 || ld_x < D || ld_q < D) return FP8B_EINVAL;
+  if (!aligned(x, 16) || ld_x % 8 != 0 || !aligned(q, 8) || ld_q % 8 != 0 || !aligned(scales, 4))
+    return FP8B_EALIGN;
+  if (T == 0) return FP8B_OK;
+  return fp8blk::launch_kv_quant(x, T, D, ld_x, q, ld_q, scales, as_stream(stream));
+}
+
+FP8B_EXPORT int fp8_kv_dequant(const uint8_t* q, int64_t T, int64_t D, int64_t ld_q, const float* scales, void* out,
+                               int64_t ld_out, void* stream) {
+  if (!q || !scales || !out) return FP8B_EINVAL;
+  if (T < 0 || T > kMaxDim || D <= 0 || D > 16384 || D % 16 != 0 || ld_q < D || ld_out < D) return FP8B_EINVAL;
+  if (!aligned(q, 16) || ld_q % 16 != 0 || !aligned(out, 16) || ld_out % 8 != 0 || !aligned(scales, 4))
+    return FP8B_EALIGN;
+  if (T == 0) return FP8B_OK;
+  return fp8blk::launch_kv_dequant(q, T, D, ld_q, scales, out, ld_out, as_stream(stream));
+}
+
 FP8B_EXPORT int fp8_cast_f32(const float* x, int64_t n, int fmt, uint8_t* q, void* stream) {
   if (fmt != FP8B_FMT_E4M3 && fmt != FP8B_FMT_E5M2) return FP8B_EUNSUPPORTED;
   if (!x || !q || n < 0) return FP8B_EINVAL;

@@ -73,16 +73,20 @@ __device__ __forceinline__ float clamp448(float v) {
   return fminf(fmaxf(v, -448.0f), 448.0f);
 }
 
-// Division by a block scale d = fp32(amax / 448), correctly rounded like
-// the IEEE quotient x / d, at a fraction of its cost.  Per block: y = 1 / d
+// Division by a block scale d = fp32(amax / Fmax) (Fmax 448 for E4M3 codes,
+// 57344 for E5M2), correctly rounded like the IEEE quotient x / d, at a
+// fraction of its cost.  Per block: y = 1 / d
 // (one IEEE division).  Per element: q = x * y, one residual r = x - q * d
 // (exact with FMA) and one correction q + r * y (Markstein's method for a
 // correctly rounded reciprocal), then the sign of x restored (the
 // correction turns (-0) into +0).  Blocks with amax < 2^-62 would put the
 // residual below fp32's normal range and use the IEEE division instead.
-// Verified exhaustively on gfx950: for every positive finite bf16 amax and
-// every bf16 x with |x| <= amax, the E4M3 code of the clamped quotient is
-// identical to the one from the IEEE division.
+// (With amax >= 2^-62 the residual of every quotient that can round to a
+// nonzero code, E4M3 or E5M2, is a normal fp32.)  Verified exhaustively on
+// gfx950 for E4M3: for every positive finite bf16 amax and every bf16 x with
+// |x| <= amax, the code of the clamped quotient is identical to the one from
+// the IEEE division; the parity tests run one block per bf16 amax for both
+// formats.
 struct BlockDivisor {
   float d, y;
   bool fast;

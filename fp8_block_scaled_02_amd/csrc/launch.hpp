@@ -16,6 +16,10 @@ int launch_act_quant(const void* x, int64_t M, int64_t K, int64_t ldx, int block
 int launch_weight_quant(const void* w, int64_t N, int64_t K, int64_t ldw, int fmt, uint8_t* q,
                         int64_t ldq, float* scales, hipStream_t s);
 int launch_cast(const float* x, int64_t n, int fmt, uint8_t* q, hipStream_t s);
+int launch_kv_quant(const void* x, int64_t T, int64_t D, int64_t ldx, uint8_t* q, int64_t ldq, float* scales,
+                    hipStream_t s);
+int launch_kv_dequant(const uint8_t* q, int64_t T, int64_t D, int64_t ldq, const float* scales, void* out,
+                      int64_t ldo, hipStream_t s);
 int launch_weight_dequant(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, const float* scales,
                           void* w, int64_t ldw, hipStream_t s);
 int launch_block_gemm(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w,

@@ -203,6 +203,87 @@ __global__ __launch_bounds__(256) void weight_dequant_kernel(
   dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
 }
 
+// KV-cache quantisation ("LLM 推理的 FP8 混合精度工程 2026", section 4: the
+// KV cache stored in E5M2 for its range, one scale per token from the
+// token's real-time amax).  One cache row (a token's K or V, D values) per
+// wave: each lane owns U 16-byte chunks (chunk lane + 64u), the row maximum
+// is reduced in-wave (DPP, then two cross-row shuffles), d = amax / 57344,
+// codes = E5M2(clamp(x / d)).  Rows past T exit; chunks past D are zeros.
+template <int U>
+__global__ __launch_bounds__(256) void kv_quant_kernel(
+    const uint16_t* __restrict__ x, int64_t T, int64_t D, int64_t ldx,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int64_t nch = D / 8;
+  uint4 raw[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t c = lane + 64 * u;
+    u32x4 v = {0, 0, 0, 0};
+    if (c < nch) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + t * ldx + 8 * c));
+    raw[u] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[i] & 0xffffu)));
+      amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xffff0000u)));
+    }
+  }
+  amax = row16_max(amax);
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  const float d = (amax == 0.0f) ? 1.0f : amax / 57344.0f;  // IEEE division
+  const BlockDivisor bd = make_divisor(amax, d);
+  if (lane == 0) scales[t] = d;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t c = lane + 64 * u;
+    if (c >= nch) continue;
+    const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = fminf(fmaxf(divide(bf16_bits_to_f32(w[i] & 0xffffu), bd), -57344.0f), 57344.0f);
+      v[2 * i + 1] = fminf(fmaxf(divide(__uint_as_float(w[i] & 0xffff0000u), bd), -57344.0f), 57344.0f);
+    }
+    uint2 out;
+    out.x = pack4_e5m2(v[0], v[1], v[2], v[3]);
+    out.y = pack4_e5m2(v[4], v[5], v[6], v[7]);
+    *reinterpret_cast<uint2*>(q + t * ldq + 8 * c) = out;
+  }
+}
+
+// KV-cache dequantisation: out = bf16_RNE(fp32(value(code) * d_t)), 16
+// codes per thread (one 16-byte load, two 16-byte stores).
+__global__ __launch_bounds__(256) void kv_dequant_kernel(
+    const uint8_t* __restrict__ q, int64_t T, int64_t D, int64_t ldq, const float* __restrict__ scales,
+    uint16_t* __restrict__ out, int64_t ldo) {
+  const int64_t cpr = D / 16;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= T * cpr) return;
+  const int64_t t = c / cpr, k = (c - t * cpr) * 16;
+  const float d = scales[t];
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q + t * ldq + k));
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8((int)v[i], 1.0f, false);  // bytes 0, 1
+    const f2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8((int)v[i], 1.0f, true);   // bytes 2, 3
+    o[2 * i] = f32_to_bf16_bits(lo[0] * d) | (f32_to_bf16_bits(lo[1] * d) << 16);
+    o[2 * i + 1] = f32_to_bf16_bits(hi[0] * d) | (f32_to_bf16_bits(hi[1] * d) << 16);
+  }
+  uint4* dst = reinterpret_cast<uint4*>(out + t * ldo + k);
+  dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 // ---- host launchers --------------------------------------------------------
 constexpr int kActUnroll = 4;
 
@@ -243,6 +324,30 @@ int launch_weight_dequant(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, c
   const dim3 grid((unsigned)((N * (K / 16) + 255) / 256));
   hipLaunchKernelGGL(weight_dequant_kernel, grid, dim3(256), 0, s, q, N, K, ldq, scales,
                      static_cast<uint16_t*>(w), ldw);
+  return check_launch();
+}
+
+int launch_kv_quant(const void* x, int64_t T, int64_t D, int64_t ldx, uint8_t* q, int64_t ldq, float* scales,
+                    hipStream_t s) {
+  const dim3 grid((unsigned)((T + 3) / 4));
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const int64_t per_lane = (D / 8 + 63) / 64;  // 16-byte chunks per lane
+#define FP8B_KV(U) hipLaunchKernelGGL(kv_quant_kernel<U>, grid, dim3(256), 0, s, xp, T, D, ldx, q, ldq, scales)
+  if (per_lane <= 1) FP8B_KV(1);
+  else if (per_lane <= 2) FP8B_KV(2);
+  else if (per_lane <= 4) FP8B_KV(4);
+  else if (per_lane <= 8) FP8B_KV(8);
+  else if (per_lane <= 16) FP8B_KV(16);
+  else FP8B_KV(32);
+#undef FP8B_KV
+  return check_launch();
+}
+
+int launch_kv_dequant(const uint8_t* q, int64_t T, int64_t D, int64_t ldq, const float* scales, void* out,
+                      int64_t ldo, hipStream_t s) {
+  const dim3 grid((unsigned)((T * (D / 16) + 255) / 256));
+  hipLaunchKernelGGL(kv_dequant_kernel, grid, dim3(256), 0, s, q, T, D, ldq, scales, static_cast<uint16_t*>(out),
+                     ldo);
   return check_launch();
 }
 

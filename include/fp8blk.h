@@ -210,6 +210,32 @@ int fp8_weight_dequant(const uint8_t *q, int64_t N, int64_t K, int64_t ld_q,
                        void *stream);
 
 /*
+ * fp8_kv_quant / fp8_kv_dequant -- KV-cache quantisation of "LLM 推理的 FP8
+ * 混合精度工程 2026", section 4 (E5M2 rather than E4M3 for the KV cache, for
+ * its range; one scale per token from the token's real-time amax, as in the
+ * section's precision table):
+ *
+ *   per row t of x [T][D] (one token's K or V):
+ *     amax = max_k |x[t][k]|,  d = fp32(amax / 57344)  (d = 1 if amax = 0),
+ *     q[t][k] = E5M2(clamp(fp32(x[t][k] / d), -57344, 57344)),  scales[t] = d;
+ *   dequantisation: out[t][k] = bf16_RNE(fp32(value(q[t][k]) * scales[t])).
+ *
+ *   T >= 0 (0 is a no-op); D in (0, 16384], D % 16 == 0.  Per-head scales:
+ *   pass the cache as T*heads rows of D = head_dim.
+ *   x       bf16 [T][ld_x], 16-byte aligned, ld_x % 8 == 0, ld_x >= D.
+ *   q       E5M2 bytes [T][ld_q], ld_q >= D; quant: 8-byte aligned,
+ *           ld_q % 8 == 0; dequant: 16-byte aligned, ld_q % 16 == 0.
+ *   scales  float [T], contiguous.
+ *   out     bf16 [T][ld_out], 16-byte aligned, ld_out % 8 == 0, >= D.
+ *   Inf codes give +-Inf, NaN codes NaN.
+ */
+int fp8_kv_quant(const void *x, int64_t T, int64_t D, int64_t ld_x,
+                 uint8_t *q, int64_t ld_q, float *scales, void *stream);
+int fp8_kv_dequant(const uint8_t *q, int64_t T, int64_t D, int64_t ld_q,
+                   const float *scales, void *out, int64_t ld_out,
+                   void *stream);
+
+/*
  * fp8_cast_f32 -- FP8Cast of "量化: FP8 与混合精度推理" (x_fp8 =
  * FP8Cast(x / s)) with s = 1: clamp each fp32 value to +-Fmax (448 for
  * E4M3, 57344 for E5M2) and round to nearest, ties to even.

@@ -26,7 +26,8 @@ def L():
 def test_header_declares_the_boundary():
     assert _declared() == sorted([
         "fp8b_abi_version", "fp8b_status_string", "fp8_act_quant", "fp8_weight_quant",
-        "fp8_block_gemm", "mxfp8_gemm", "fp8_grouped_gemm", "fp8_weight_dequant", "fp8_cast_f32"])
+        "fp8_block_gemm", "mxfp8_gemm", "fp8_grouped_gemm", "fp8_weight_dequant", "fp8_kv_quant", "fp8_kv_dequant",
+        "fp8_cast_f32"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -81,6 +82,21 @@ def test_weight_dequant_validation(L):
     assert f(ODD, 256, 256, 256, GOOD, GOOD, 256, NULL) == -2
     assert f(GOOD, 256, 256, 264, GOOD, GOOD, 256, NULL) == -2           # ld_q % 16
     assert f(GOOD, 256, 256, 256, GOOD, GOOD, 260, NULL) == -2           # ld_w % 8
+
+
+def test_kv_validation(L):
+    f = L.fp8_kv_quant
+    assert f(NULL, 4, 1024, 1024, GOOD, 1024, GOOD, NULL) == -1
+    assert f(GOOD, 4, 1000, 1000, GOOD, 1024, GOOD, NULL) == -1          # D % 16
+    assert f(GOOD, 4, 32768, 32768, GOOD, 32768, GOOD, NULL) == -1       # D > 16384
+    assert f(GOOD, 4, 1024, 512, GOOD, 1024, GOOD, NULL) == -1           # ld_x < D
+    assert f(ODD, 4, 1024, 1024, GOOD, 1024, GOOD, NULL) == -2
+    assert f(GOOD, 4, 1024, 1028, GOOD, 1024, GOOD, NULL) == -2          # ld_x % 8
+    assert f(GOOD, 0, 1024, 1024, GOOD, 1024, GOOD, NULL) == 0           # T = 0
+    g = L.fp8_kv_dequant
+    assert g(GOOD, 4, 1024, 1024, NULL, GOOD, 1024, NULL) == -1
+    assert g(GOOD, 4, 1024, 1032, GOOD, GOOD, 1024, NULL) == -2          # ld_q % 16
+    assert g(GOOD, 0, 1024, 1024, GOOD, GOOD, 1024, NULL) == 0
 
 
 def test_block_gemm_validation(L):

@@ -240,3 +240,56 @@ def test_weight_dequant_prefill_full(F, orc, fmt):
     w = F.fp8_weight_dequant(wq, ws)
     torch.cuda.synchronize()
     _deq_check(_np(w.view(torch.int16)).view(np.uint16), orc.weight_dequant(_np(wq), _np(ws)), f"18432x7168 {fmt}")
+
+
+# ---- KV cache (E5M2, one scale per row) ----------------------------------------
+def _kv_run(F, orc, x, what):
+    q, s = F.fp8_kv_quant(x.to(DEV))
+    torch.cuda.synchronize()
+    q2, s2 = orc.kv_quant(W.bits(x))
+    _assert_same(_np(q), _np(s), q2, s2, what)
+    return q, s, q2, s2
+
+
+@pytest.mark.parametrize("T,D", [(1, 16), (7, 128), (5, 576), (9, 1024), (3, 4096), (6, 8192), (2, 16384), (130, 1040)])
+def test_kv_quant_shapes(F, orc, T, D):
+    g = W.gen(T * 7 + D)
+    _kv_run(F, orc, W.kv_rows(T, D, g), f"kv {T}x{D}")
+
+
+def test_kv_quant_every_row_magnitude(F, orc):
+    """One row per bf16 amax pattern (every exponent incl. subnormals): the row
+    holds amax, -amax, -0, a value deep in the E5M2 subnormal codes and random
+    in-range values, so the scale division spans the whole fp32 range."""
+    amax = (np.arange(1, 0x7F80, dtype=np.uint32) << 16).view(np.float32)
+    rng = np.random.default_rng(19)
+    vals = rng.uniform(-1, 1, size=(len(amax), 128)).astype(np.float32) * amax[:, None]
+    vals[:, 0], vals[:, 1], vals[:, 2] = amax, -amax, -0.0
+    vals[:, 3] = amax * np.float32(2.0 ** -30)
+    x = torch.from_numpy(vals).to(torch.bfloat16)
+    _kv_run(F, orc, x, "every amax row")
+
+
+def test_kv_quant_full_and_dequant(F, orc):
+    c = W.CONFIGS["kv"]
+    x = W.kv_rows(c["T"], c["D"], W.gen(12, DEV))
+    q, s, q2, s2 = _kv_run(F, orc, x, "kv 32768x1024")
+    out = F.fp8_kv_dequant(q, s)
+    torch.cuda.synchronize()
+    _deq_check(_np(out.view(torch.int16)).view(np.uint16), orc.kv_dequant(q2, s2), "kv dequant full")
+
+
+def test_kv_dequant_every_code_and_strides(F, orc):
+    rng = np.random.default_rng(23)
+    q = rng.integers(0, 256, size=(64, 512), dtype=np.uint8)
+    q[0, :256] = np.arange(256, dtype=np.uint8)
+    s = np.exp(rng.uniform(-87, 87, size=64)).astype(np.float32)
+    s[1], s[2] = 2.0 ** -140, 1.0
+    qd = torch.zeros(64, 528, dtype=torch.uint8, device=DEV)
+    qd[:, :512] = torch.from_numpy(q).to(DEV)
+    out = torch.full((64, 520), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    F.fp8_kv_dequant(qd[:, :512], torch.from_numpy(s).to(DEV), out=out[:, :512])
+    torch.cuda.synchronize()
+    o = _np(out.view(torch.int16)).view(np.uint16)
+    assert (o[:, 512:] == 0xFFFF).all()
+    _deq_check(o[:, :512], orc.kv_dequant(q, s), "kv dequant codes")
