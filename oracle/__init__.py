@@ -64,6 +64,7 @@ def lib():
         L.orc_weight_dequant.argtypes = [_c_u8p, _i64, _i64, _i64, _c_f32p, _c_u16p, _i64]
         L.orc_kv_quant.argtypes = [_c_u16p, _i64, _i64, _i64, _c_u8p, _i64, _c_f32p]
         L.orc_kv_dequant.argtypes = [_c_u8p, _i64, _i64, _i64, _c_f32p, _c_u16p, _i64]
+        L.orc_moe_combine.argtypes = [_c_u16p, _i64, _i64, _c_i32p, _c_f32p, _i64, _i64, _c_f64p, _c_f64p]
         L.orc_weight_quant.argtypes = [_c_u16p, _i64, _i64, _i64, ctypes.c_int,
                                        _c_u8p, _i64, _c_f32p]
         L.orc_block_gemm.argtypes = [_c_u8p, _i64, _c_f32p, _c_u8p, _i64, _c_f32p,
@@ -194,6 +195,22 @@ def kv_dequant(q, scales):
     if lib().orc_kv_dequant(_p(q, _c_u8p), T, D, D, _p(s, _c_f32p), _p(out, _c_u16p), D) != 0:
         raise ValueError("orc_kv_dequant rejected its arguments")
     return out
+
+
+def moe_combine(y_bits, token_rows, gates):
+    """y bf16 bits [R, N], token_rows int32 [T, k], gates fp32 [T, k] ->
+    (out fp64 [T, N], bound fp64 [T, N])."""
+    y = _c(y_bits, np.uint16)
+    tr = _c(token_rows, np.int32)
+    g = _c(gates, np.float32)
+    R, N = y.shape
+    T, k = tr.shape
+    out = np.empty((T, N), np.float64)
+    b = np.empty((T, N), np.float64)
+    if lib().orc_moe_combine(_p(y, _c_u16p), R, N, _p(tr, _c_i32p), _p(g, _c_f32p), T, k,
+                             _p(out, _c_f64p), _p(b, _c_f64p)) != 0:
+        raise ValueError("orc_moe_combine rejected its arguments")
+    return out, b
 
 
 # ---- GEMM references -----------------------------------------------------

@@ -340,6 +340,40 @@ int orc_kv_dequant(const uint8_t *q, int64_t T, int64_t D, int64_t ldq, const fl
 }
 
 /* ------------------------------------------------------------------------ */
+/* MoE combine.  [P1] section 2 (block-scale fused MoE) and the DeepSeek-V3 */
+/* guide's 8 active experts per token: after the grouped GEMM, each token's */
+/* output is the gate-weighted sum of its routed rows.  The gate weights    */
+/* and the (token, slot) -> routed-row map are inputs (the model's gating   */
+/* function is not part of the method).  Reference: the exact sum in fp64  */
+/* (each product of a bf16 and an fp32 is exact in fp64; k <= 16 terms are */
+/* summed in fp64), plus the bound sum |gate * y| for tolerance checks.     */
+/* ------------------------------------------------------------------------ */
+int orc_moe_combine(const uint16_t *y, int64_t R, int64_t N, const int32_t *token_rows,
+                    const float *gates, int64_t T, int64_t topk, double *out, double *bnd) {
+  int64_t t;
+  if (!y || !token_rows || !gates || !out || !bnd || R < 0 || N <= 0 || T < 0 || topk < 1)
+    return -1;
+  for (t = 0; t < T * topk; ++t)
+    if (token_rows[t] < 0 || token_rows[t] >= R) return -1;
+#pragma omp parallel for schedule(static)
+  for (t = 0; t < T; ++t) {
+    int64_t n, j;
+    for (n = 0; n < N; ++n) {
+      double acc = 0.0, b = 0.0;
+      for (j = 0; j < topk; ++j) {
+        const int64_t r = token_rows[t * topk + j];
+        const double p = (double)gates[t * topk + j] * (double)bf16_to_f32(y[r * N + n]);
+        acc += p;
+        b += fabs(p);
+      }
+      out[t * N + n] = acc;
+      bnd[t * N + n] = b;
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* GEMM references.  [P2] section 3: FP8 x FP8 products accumulated in FP32 */
 /* with per-block scales; [P4]: fp8_gemm(x, scale, weight, weight.scale).   */
 /* Here the inner products are exact: 512 * val(code) is an integer for    */

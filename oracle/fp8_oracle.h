@@ -11,8 +11,9 @@
  *  [P1] "ROCm 7.0 FP8/MXFP8/MXFP4" article (devpress.csdn.net, AMD channel),
  *       section 1.1 (format table: E4M3 max 448, E5M2 max 57344, MXFP8 =
  *       8 bit + shared exponent), section 1.2 (MXFP8: 32-element blocks, one
- *       scale each), and the "Delayed Scaling" listing of the training part
- *       (order of operations: divide by the scale, clamp to +-448, cast).
+ *       scale each), section 2 (block-scale fused MoE operator), and the
+ *       "Delayed Scaling" listing of the training part (order of operations:
+ *       divide by the scale, clamp to +-448, cast).
  *  [P2] "LLM 推理的 FP8 混合精度工程 2026" (blog.lonae.com), section 2
  *       (quantizer Q(x) = clamp(round(x*s), -Fmax, Fmax) * s^-1, Fmax 448 /
  *       57344), section 3 (FP32 accumulation, 128x128 blockwise scales) and
@@ -103,6 +104,14 @@ int orc_kv_quant(const uint16_t *x, int64_t T, int64_t D, int64_t ldx, uint8_t *
                  int64_t ldq, float *scales);
 int orc_kv_dequant(const uint8_t *q, int64_t T, int64_t D, int64_t ldq, const float *scales,
                    uint16_t *out, int64_t ldo);
+
+/* ---- MoE combine ([P1] section 2, fused MoE; 8 active experts per token) --
+ * out[t][n] = sum_j gates[t][j] * y[token_rows[t][j]][n] (fp64, exact
+ * products), bnd[t][n] = sum_j |gates[t][j] * y[...][n]|.  y is bf16 bits
+ * [R][N]; gates fp32 [T][topk]; token_rows int32 [T][topk] in [0, R).
+ * Returns 0, or -1 on bad arguments (including a row outside [0, R)). */
+int orc_moe_combine(const uint16_t *y, int64_t R, int64_t N, const int32_t *token_rows,
+                    const float *gates, int64_t T, int64_t topk, double *out, double *bnd);
 
 /* ---- block-scaled GEMM reference: y[m][n] = sum_kb sa[m][kb] *
  * sw[n/128][kb] * sum_{k in kb} val(a[m][k]) * val(w[n][k]).

@@ -17,7 +17,10 @@ their shapes and value structure):
   per (row, 32-element K block);
 * MoE routing: logits z ~ N(0, 1) plus a per-expert bias -s*ln(rank) (Zipf
   skew, s = 1 by default), top-k by logit with ties to the lower expert id,
-  rows ordered by (expert, token, slot).
+  rows ordered by (expert, token, slot); gate weights for the combine are a
+  softmax over each token's chosen logits (the model's gating function is
+  an input to the method, not part of it);
+* KV-cache rows: bf16(z * 2^u), u ~ U(-8, 8) per token.
 """
 from dataclasses import dataclass
 import math
@@ -26,7 +29,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "bits", "gen", "activations", "weights", "mx_operand", "routing",
+    "bits", "gen", "activations", "weights", "mx_operand", "kv_rows", "routing", "routing_full",
     "LinearCase", "tiny_linear", "decode_linear", "prefill_linear",
     "mx_case", "moe_case", "CONFIGS",
 ]
@@ -97,9 +100,15 @@ def kv_rows(T: int, D: int, g: torch.Generator, lo: float = -8.0, hi: float = 8.
     return (z * torch.exp2(u)).to(torch.bfloat16)
 
 
-def routing(T: int, E: int, topk: int, s: float, g: torch.Generator):
-    """Top-k MoE routing (CPU).  Returns (row_index int32 [T*topk],
-    expert_offsets int32 [E+1], per-row expert id int32 [T*topk])."""
+def routing_full(T: int, E: int, topk: int, s: float, g: torch.Generator) -> dict:
+    """Top-k MoE routing (CPU) with the combine inputs:
+    row_index int32 [R]   token of each routed row (rows ordered by
+                          (expert, token, slot)),
+    offs      int32 [E+1] expert offsets into the routed rows,
+    experts   int32 [R]   expert of each routed row,
+    token_rows int32 [T, topk] routed row of (token, slot),
+    gates     fp32 [T, topk]  gate weight of (token, slot): softmax over the
+                          token's chosen logits (fp32)."""
     assert g.device.type == "cpu"
     z = torch.randn(T, E, generator=g, dtype=torch.float32)
     rank = torch.randperm(E, generator=g) + 1            # 1..E
@@ -117,7 +126,18 @@ def routing(T: int, E: int, topk: int, s: float, g: torch.Generator):
     counts = torch.bincount(experts.to(torch.int64), minlength=E)
     offs = torch.zeros(E + 1, dtype=torch.int32)
     offs[1:] = torch.cumsum(counts, 0).to(torch.int32)
-    return row_index, offs, experts
+    token_rows = torch.empty(T * topk, dtype=torch.int32)
+    token_rows[perm] = torch.arange(T * topk, dtype=torch.int32)
+    gates = torch.softmax(torch.gather(logits, 1, chosen), dim=1)
+    return dict(row_index=row_index, offs=offs, experts=experts,
+                token_rows=token_rows.view(T, topk), gates=gates.contiguous())
+
+
+def routing(T: int, E: int, topk: int, s: float, g: torch.Generator):
+    """Top-k MoE routing (CPU).  Returns (row_index int32 [T*topk],
+    expert_offsets int32 [E+1], per-row expert id int32 [T*topk])."""
+    r = routing_full(T, E, topk, s, g)
+    return r["row_index"], r["offs"], r["experts"]
 
 
 @dataclass
