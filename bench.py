@@ -279,10 +279,19 @@ def run_legs(torch, F, W, dev, only=""):
         counts = (case.offs[1:] - case.offs[:-1])
         active = int((counts > 0).sum())
         nbytes = active * (N * K + (N // 128) * (K // 128) * 4) + T * (K + K // 128 * 4) + R * N * 2
+        # the whole projection: act_quant, grouped GEMM, gate-weighted combine
+        rt = W.routing_full(T, E, case.row_index.shape[0] // T, 1.0, W.gen(4, "cpu"))
+        tr, gt = rt["token_rows"].to(dev), rt["gates"].to(dev)
+        out = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+        t_c = timed(torch, lambda: F.fp8_moe_combine(y, tr, gt, torch.bfloat16, out=out), iters)
+        t_l = timed(torch, lambda: F.moe_forward(case.x, ri, offs, tr, gt, wq, ws), iters)
+        cbytes = R * N * 2 + T * N * 2 + R * 8
         legs["moe"] = {"us": round(t * 1e6, 2), "TFLOPs": round(2.0 * R * N * K / t / 1e12, 1),
                        "GBps": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
-                       "active_experts": active, "max_rows": int(counts.max())}
-        del wq, ws, a, sa, y
+                       "active_experts": active, "max_rows": int(counts.max()),
+                       "combine_us": round(t_c * 1e6, 2), "combine_GBps": round(cbytes / t_c / 1e9, 1),
+                       "layer_us": round(t_l * 1e6, 2), "layer_TFLOPs": round(2.0 * R * N * K / t_l / 1e12, 1)}
+        del wq, ws, a, sa, y, out, tr, gt
         torch.cuda.empty_cache()
     if only in ("", "dequant"):
         c = W.prefill_linear(device=dev)

@@ -64,6 +64,8 @@ def lib():
         L.fp8_grouped_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp, i64, i64, vp, ci, vp]
         L.fp8_weight_dequant.restype = ci
         L.fp8_weight_dequant.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp]
+        L.fp8_moe_combine.restype = ci
+        L.fp8_moe_combine.argtypes = [vp, i64, i64, vp, vp, i64, i64, vp, ci, vp]
         L.fp8_kv_quant.restype = ci
         L.fp8_kv_quant.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
         L.fp8_kv_dequant.restype = ci
@@ -152,6 +154,36 @@ def fp8_weight_dequant(q: torch.Tensor, scales: torch.Tensor, w=None):
     rc = lib().fp8_weight_dequant(_p(q), N, K, q.stride(0), _p(scales), _p(w), w.stride(0), _stream(q))
     _check("fp8_weight_dequant", rc)
     return w
+
+
+def fp8_moe_combine(y: torch.Tensor, token_rows: torch.Tensor, gates: torch.Tensor, out_dtype=torch.bfloat16,
+                    out=None):
+    """out[t] = sum_j gates[t, j] * y[token_rows[t, j]] (fp32 accumulation):
+    y bf16 [R, N] routed rows, token_rows int32 [T, k], gates fp32 [T, k]."""
+    _need(y.dtype == torch.bfloat16 and y.dim() == 2 and y.is_contiguous(), "y must be contiguous 2-D bf16")
+    _need(token_rows.dtype == torch.int32 and token_rows.is_contiguous(), "token_rows must be contiguous int32")
+    _need(gates.dtype == torch.float32 and gates.is_contiguous(), "gates must be contiguous float32")
+    _need(token_rows.shape == gates.shape and token_rows.dim() == 2, "token_rows and gates must be [T, k]")
+    R, N = y.shape
+    T, k = token_rows.shape
+    od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    if out is None:
+        out = torch.empty(T, N, dtype=out_dtype, device=y.device)
+    _need(out.is_contiguous() and out.dtype == out_dtype, "out must be contiguous of out_dtype")
+    rc = lib().fp8_moe_combine(_p(y), R, N, _p(token_rows), _p(gates), T, k, _p(out), od, _stream(y))
+    _check("fp8_moe_combine", rc)
+    return out
+
+
+def moe_forward(x: torch.Tensor, row_index, expert_offsets, token_rows, gates, w_q, w_scales,
+                out_dtype=torch.bfloat16):
+    """One block-scale MoE expert projection as a kernel sequence: act_quant
+    of the tokens (once per token, per 128 channels, fp32 scales), the
+    grouped GEMM over the routed rows (gather inside), then the gate-weighted
+    combine back to tokens.  Returns (out [T, N], y routed rows [R, N])."""
+    a, sa = fp8_act_quant(x, 128, "fp32")
+    y = fp8_grouped_gemm(a, sa, row_index, expert_offsets, w_q, w_scales, torch.bfloat16)
+    return fp8_moe_combine(y, token_rows, gates, out_dtype), y
 
 
 def fp8_kv_quant(x: torch.Tensor, q=None, scales=None):

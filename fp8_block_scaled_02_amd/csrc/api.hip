@@ -111,6 +111,19 @@ FP8B_EXPORT int fp8_weight_dequant(const uint8_t* q, int64_t N, int64_t K, int64
   return fp8blk::launch_weight_dequant(q, N, K, ld_q, scales, w, ld_w, as_stream(stream));
 }
 
+FP8B_EXPORT int fp8_moe_combine(const void* y, int64_t R, int64_t N, const int32_t* token_rows, const float* gates,
+                                int64_t T, int64_t topk, void* out, int out_dtype, void* stream) {
+  if (out_dtype != FP8B_OUT_F32 && out_dtype != FP8B_OUT_BF16) return FP8B_EUNSUPPORTED;
+  if (!y || !token_rows || !gates || !out) return FP8B_EINVAL;
+  if (R < 1 || R > kMaxDim || N <= 0 || N > kMaxDim || N % 8 != 0 || T < 0 || T > kMaxDim) return FP8B_EINVAL;
+  if (topk < 1 || topk > 64) return FP8B_EINVAL;
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(token_rows, 4) || !aligned(gates, 4)) return FP8B_EALIGN;
+  if (T * (N / 8) / 256 >= INT32_MAX) return FP8B_EINVAL;
+  if (T == 0) return FP8B_OK;
+  return fp8blk::launch_moe_combine(y, R, N, token_rows, gates, T, topk, out, out_dtype == FP8B_OUT_BF16,
+                                    as_stream(stream));
+}
+
 FP8B_EXPORT int fp8_kv_quant(const void* x, int64_t T, int64_t D, int64_t ld_x, uint8_t* q, int64_t ld_q, float* scales,
                              void* stream) {
   if (!x || !q || !scales) return FP8B_EINVAL;

@@ -190,6 +190,31 @@ int fp8_grouped_gemm(const uint8_t *a, const float *a_scales, int64_t T,
                      int out_dtype, void *stream);
 
 /*
+ * fp8_moe_combine -- the gate-weighted combine after fp8_grouped_gemm,
+ * closing a block-scale MoE layer (ROCm 7.0 FP8 article, section 2: the
+ * block-scale fused MoE operator; the DeepSeek-V3 guide: 8 active experts
+ * per token):
+ *
+ *   out[t][n] = sum_{j < topk} gates[t][j] * y[token_rows[t][j]][n]
+ *   accumulated in fp32 in slot order (one fused multiply-add per slot),
+ *   written as fp32 or bf16 (nearest even).
+ *
+ *   y           bf16 [R][N] (the grouped GEMM's rows in routed order),
+ *               contiguous, 16-byte aligned; R >= 1.
+ *   N           > 0, N % 8 == 0.
+ *   token_rows  int32 [T][topk]: routed row of (token, slot); rows outside
+ *               [0, R) give unspecified outputs but never fault.
+ *   gates       float [T][topk] gate weights (the model's gating function
+ *               is the caller's).
+ *   T >= 0 (0 is a no-op); 1 <= topk <= 64.
+ *   out         [T][N] fp32 or bf16, contiguous, 16-byte aligned.
+ *   out_dtype   FP8B_OUT_F32 or FP8B_OUT_BF16.
+ */
+int fp8_moe_combine(const void *y, int64_t R, int64_t N,
+                    const int32_t *token_rows, const float *gates, int64_t T,
+                    int64_t topk, void *out, int out_dtype, void *stream);
+
+/*
  * fp8_weight_dequant -- weight dequantisation, the bf16 branch of the
  * DeepSeek-V3 guide's dispatch snippet (weight_dequant(weight,
  * weight.scale), used to turn the FP8 checkpoint into bf16) and

@@ -47,8 +47,8 @@ def check_bf16(y, y_ref, bnd, rel=REL):
     return ok, float(np.max(ratio)) if ratio.size else 0.0
 
 
-def assert_parity(y, y_ref, bnd, bf16: bool, what=""):
-    ok, worst = (check_bf16 if bf16 else check_f32)(y, y_ref, bnd)
+def assert_parity(y, y_ref, bnd, bf16: bool, what="", rel=REL):
+    ok, worst = (check_bf16 if bf16 else check_f32)(y, y_ref, bnd, rel)
     if not ok.all():
         idx = np.argwhere(~ok)
         i = tuple(idx[0])

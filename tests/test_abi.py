@@ -26,7 +26,7 @@ def L():
 def test_header_declares_the_boundary():
     assert _declared() == sorted([
         "fp8b_abi_version", "fp8b_status_string", "fp8_act_quant", "fp8_weight_quant",
-        "fp8_block_gemm", "mxfp8_gemm", "fp8_grouped_gemm", "fp8_weight_dequant", "fp8_kv_quant", "fp8_kv_dequant",
+        "fp8_block_gemm", "mxfp8_gemm", "fp8_grouped_gemm", "fp8_moe_combine", "fp8_weight_dequant", "fp8_kv_quant", "fp8_kv_dequant",
         "fp8_cast_f32"])
 
 
@@ -82,6 +82,23 @@ def test_weight_dequant_validation(L):
     assert f(ODD, 256, 256, 256, GOOD, GOOD, 256, NULL) == -2
     assert f(GOOD, 256, 256, 264, GOOD, GOOD, 256, NULL) == -2           # ld_q % 16
     assert f(GOOD, 256, 256, 256, GOOD, GOOD, 260, NULL) == -2           # ld_w % 8
+
+
+def test_moe_combine_validation(L):
+    f = L.fp8_moe_combine
+    args = [GOOD, 64, 256, GOOD, GOOD, 8, 8, GOOD, 1, NULL]
+    bad = list(args); bad[8] = 5
+    assert f(*bad) == -3
+    bad = list(args); bad[2] = 100
+    assert f(*bad) == -1                                                  # N % 8
+    bad = list(args); bad[6] = 0
+    assert f(*bad) == -1                                                  # topk
+    bad = list(args); bad[1] = 0
+    assert f(*bad) == -1                                                  # R = 0
+    bad = list(args); bad[0] = ODD
+    assert f(*bad) == -2
+    bad = list(args); bad[5] = 0
+    assert f(*bad) == 0                                                   # T = 0
 
 
 def test_kv_validation(L):

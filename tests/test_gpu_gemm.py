@@ -278,3 +278,56 @@ def test_mx_gemm_applies_block_exponents_exactly(F, orc):
     y = F.mxfp8_gemm(*[torch.from_numpy(v).to(DEV) for v in (a, ea, b, eb)])
     want = tab[a] * np.ldexp(1.0, np.repeat(ea.astype(int) - 127, 32, axis=1))
     np.testing.assert_array_equal(_np(y), want)
+
+
+# ---- MoE combine ---------------------------------------------------------------
+def _combine_check(F, orc, y, tr, gates, out_dtype, what):
+    out = F.fp8_moe_combine(y, tr, gates, out_dtype)
+    torch.cuda.synchronize()
+    ref, bnd = orc.moe_combine(y.view(torch.int16).cpu().numpy().view(np.uint16),
+                               tr.cpu().numpy(), gates.cpu().numpy())
+    k = tr.shape[1]
+    # fp32 accumulation of k exact products: at most k roundings of 2^-24
+    return assert_parity(_np(out), ref, bnd, out_dtype == torch.bfloat16, what, rel=k * 2.0 ** -24)
+
+
+@pytest.mark.parametrize("T,E,k,N", [(64, 8, 4, 256), (1, 4, 1, 8), (37, 16, 8, 136), (300, 64, 6, 1024)])
+def test_moe_combine_small(F, orc, T, E, k, N):
+    r = W.routing_full(T, E, k, 1.0, W.gen(T + N))
+    R = T * k
+    y = torch.randn(R, N, generator=W.gen(k), dtype=torch.float32).to(torch.bfloat16).to(DEV)
+    tr, g = r["token_rows"].to(DEV), r["gates"].to(DEV)
+    _combine_check(F, orc, y, tr, g, torch.float32, f"combine f32 {T}x{k}x{N}")
+    _combine_check(F, orc, y, tr, g, torch.bfloat16, f"combine bf16 {T}x{k}x{N}")
+
+
+def test_moe_forward_full(F, orc):
+    """The whole expert projection at 4096 tokens x 256 experts (top-8): the
+    routed rows are checked on sampled rows against the oracle's grouped
+    GEMM, and every token's combine against the oracle's combine of them."""
+    case = W.moe_case(device=DEV)
+    r = W.routing_full(4096, 256, 8, 1.0, W.gen(4, "cpu"))
+    assert torch.equal(r["row_index"], case.row_index)
+    E, N, K = case.w.shape
+    wq = torch.empty(E, N, K, dtype=torch.uint8, device=DEV)
+    ws = torch.empty(E, N // 128, K // 128, dtype=torch.float32, device=DEV)
+    for e in range(E):
+        F.fp8_weight_quant(case.w[e], "fp32", q=wq[e], scales=ws[e])
+    tr, g = r["token_rows"].to(DEV), r["gates"].to(DEV)
+    out, y = F.moe_forward(case.x, case.row_index.to(DEV), case.offs.to(DEV), tr, g, wq, ws)
+    torch.cuda.synchronize()
+    worst = _combine_check(F, orc, y, tr, g, torch.bfloat16, "moe combine 4096x2048")
+    # the routed rows of two tokens, against the oracle GEMM
+    rows = sorted(set(r["token_rows"][0].tolist()) | set(r["token_rows"][4095].tolist()))
+    offs = case.offs.numpy()
+    toks = sorted({int(case.row_index[q]) for q in rows})
+    oa_full = np.zeros((case.x.shape[0], K), np.uint8)
+    osa_full = np.ones((case.x.shape[0], K // 128), np.float32)
+    oa, osa = orc.act_quant(W.bits(case.x[torch.as_tensor(toks, device=case.x.device)]), 128, 0)
+    oa_full[toks], osa_full[toks] = oa, osa
+    wl, sl = [None] * E, [None] * E
+    for e in sorted({int(np.searchsorted(offs, q, side="right") - 1) for q in rows}):
+        wl[e], sl[e] = orc.weight_quant(W.bits(case.w[e]), 0)
+    yr, bnd = orc.grouped_gemm(oa_full, osa_full, case.row_index.numpy(), offs, wl, sl, rows=np.asarray(rows))
+    assert_parity(_np(y[torch.as_tensor(rows, device=DEV)]), yr, bnd, True, "moe routed rows")
+    print(f"moe combine worst {worst:.3g}")
