@@ -65,6 +65,7 @@ def lib():
         L.orc_kv_quant.argtypes = [_c_u16p, _i64, _i64, _i64, _c_u8p, _i64, _c_f32p]
         L.orc_kv_dequant.argtypes = [_c_u8p, _i64, _i64, _i64, _c_f32p, _c_u16p, _i64]
         L.orc_moe_combine.argtypes = [_c_u16p, _i64, _i64, _c_i32p, _c_f32p, _i64, _i64, _c_f64p, _c_f64p]
+        L.orc_delayed_scaling.argtypes = [_c_u16p, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float, _c_u8p, _c_f32p]
         L.orc_weight_quant.argtypes = [_c_u16p, _i64, _i64, _i64, ctypes.c_int,
                                        _c_u8p, _i64, _c_f32p]
         L.orc_block_gemm.argtypes = [_c_u8p, _i64, _c_f32p, _c_u8p, _i64, _c_f32p,
@@ -211,6 +212,19 @@ def moe_combine(y_bits, token_rows, gates):
                              _p(out, _c_f64p), _p(b, _c_f64p)) != 0:
         raise ValueError("orc_moe_combine rejected its arguments")
     return out, b
+
+
+def delayed_scaling(x_bits, history_len: int, algo: int, divisor: float = 400.0):
+    """x_bits uint16 [S, n] (one bf16 tensor per step) -> (codes [S, n],
+    scales used per step fp32 [S])."""
+    x = _c(x_bits, np.uint16)
+    S, n = x.shape
+    q = np.empty((S, n), np.uint8)
+    sc = np.empty(S, np.float32)
+    if lib().orc_delayed_scaling(_p(x, _c_u16p), S, n, history_len, algo, divisor, _p(q, _c_u8p),
+                                 _p(sc, _c_f32p)) != 0:
+        raise ValueError("orc_delayed_scaling rejected its arguments")
+    return q, sc
 
 
 # ---- GEMM references -----------------------------------------------------

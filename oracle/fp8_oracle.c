@@ -374,6 +374,56 @@ int orc_moe_combine(const uint16_t *y, int64_t R, int64_t N, const int32_t *toke
 }
 
 /* ------------------------------------------------------------------------ */
+/* Delayed scaling.  [P1] "Delayed Scaling" (training part): the current     */
+/* step is quantised with the scale derived from earlier steps (code =       */
+/* E4M3(clamp(x / scale, +-448))), then the scale for the next step is set   */
+/* from the current tensor's amax with a safety margin (amax / 400); the     */
+/* initial scale is 1.  [P1] pitfall section: an amax history window         */
+/* (amax_history_len) and a compute algorithm "max" (the window maximum      */
+/* rather than the latest value).  Readings: one scale per tensor; the       */
+/* history holds the last L amaxes (fewer at the start); algo 0 = window     */
+/* maximum, algo 1 = latest; next scale = fp32(h / divisor) with one IEEE    */
+/* division, or 1 when h = 0.                                                */
+/* ------------------------------------------------------------------------ */
+int orc_delayed_scaling(const uint16_t *x, int64_t S, int64_t n, int64_t L, int algo,
+                        float divisor, uint8_t *q, float *scales_used) {
+  int64_t s, i;
+  float scale = 1.0f;
+  float *hist;
+  int64_t filled = 0, pos = 0;
+  if (!x || !q || !scales_used || S < 0 || n <= 0 || L < 1 || (algo != 0 && algo != 1) ||
+      !(divisor > 0.0f))
+    return -1;
+  hist = (float *)calloc((size_t)L, sizeof(float));
+  if (!hist) return -1;
+  for (s = 0; s < S; ++s) {
+    const uint16_t *xs = x + s * n;
+    float amax = 0.0f, h = 0.0f;
+    scales_used[s] = scale;
+    for (i = 0; i < n; ++i) {
+      float v = bf16_to_f32(xs[i]);
+      float t = v / scale;               /* fp32 quotient */
+      if (t > 448.0f) t = 448.0f;
+      if (t < -448.0f) t = -448.0f;
+      q[s * n + i] = orc_e4m3_encode(t);
+      if (fabsf(v) > amax) amax = fabsf(v);
+    }
+    hist[pos] = amax;
+    pos = (pos + 1) % L;
+    if (filled < L) ++filled;
+    if (algo == 1) {
+      h = amax;
+    } else {
+      for (i = 0; i < filled; ++i)
+        if (hist[i] > h) h = hist[i];
+    }
+    scale = (h == 0.0f) ? 1.0f : h / divisor;
+  }
+  free(hist);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* GEMM references.  [P2] section 3: FP8 x FP8 products accumulated in FP32 */
 /* with per-block scales; [P4]: fp8_gemm(x, scale, weight, weight.scale).   */
 /* Here the inner products are exact: 512 * val(code) is an integer for    */

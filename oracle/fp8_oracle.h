@@ -113,6 +113,15 @@ int orc_kv_dequant(const uint8_t *q, int64_t T, int64_t D, int64_t ldq, const fl
 int orc_moe_combine(const uint16_t *y, int64_t R, int64_t N, const int32_t *token_rows,
                     const float *gates, int64_t T, int64_t topk, double *out, double *bnd);
 
+/* ---- delayed scaling ([P1] "Delayed Scaling"; amax history, algo "max") ---
+ * Runs S steps over x [S][n] (bf16 bits) from the initial state (scale 1,
+ * empty history of length L): step s writes q[s] = E4M3(clamp(fp32(x[s] /
+ * scale), +-448)) and scales_used[s] = scale, then pushes amax(x[s]) into
+ * the history and sets scale = fp32(h / divisor) (1 if h = 0), h the
+ * history maximum (algo 0) or the latest amax (algo 1). */
+int orc_delayed_scaling(const uint16_t *x, int64_t S, int64_t n, int64_t L, int algo,
+                        float divisor, uint8_t *q, float *scales_used);
+
 /* ---- block-scaled GEMM reference: y[m][n] = sum_kb sa[m][kb] *
  * sw[n/128][kb] * sum_{k in kb} val(a[m][k]) * val(w[n][k]).
  * Inner sums are exact integers (val * 2^9 is an integer for every finite
