@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--no-legs", action="store_true", help="time the headline step only")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
-    p.add_argument("--only", default="", help="run one leg only: decode|mx|moe|dequant|kv")
+    p.add_argument("--only", default="", help="run one leg only: decode|mx|moe|dequant|kv|delayed")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (a kernel of known traffic, for "
                         "scaling profiler byte counters)")
@@ -317,6 +317,20 @@ def run_legs(torch, F, W, dev, only=""):
         legs["kv_cache"] = {"shape": [T, D], "quant_us": round(t_q * 1e6, 2), "quant_GBps": round(nbytes / t_q / 1e9, 1),
                             "dequant_us": round(t_d * 1e6, 2), "dequant_GBps": round(nbytes / t_d / 1e9, 1)}
         del x, q, sc, out
+        torch.cuda.empty_cache()
+    if only in ("", "delayed"):
+        c = W.prefill_linear(device=dev)
+        x = c.x
+        n = x.numel()
+        del c
+        ds = F.DelayedScaler(16, "max", 400.0, device=dev)
+        q = torch.empty(n, dtype=torch.uint8, device=dev)
+        su = torch.empty(1, dtype=torch.float32, device=dev)
+        t = timed(torch, lambda: ds.quantize(x, q=q, scale_used=su), iters)
+        nbytes = n * 3
+        legs["delayed_scaling"] = {"shape": list(x.shape), "us": round(t * 1e6, 2),
+                                   "GBps": round(nbytes / t / 1e9, 1)}
+        del x, q, su, ds
         torch.cuda.empty_cache()
     return legs
 

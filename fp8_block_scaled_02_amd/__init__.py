@@ -70,6 +70,10 @@ def lib():
         L.fp8_kv_quant.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
         L.fp8_kv_dequant.restype = ci
         L.fp8_kv_dequant.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp]
+        L.fp8_delayed_state_init.restype = ci
+        L.fp8_delayed_state_init.argtypes = [vp, i64, vp]
+        L.fp8_delayed_quant.restype = ci
+        L.fp8_delayed_quant.argtypes = [vp, i64, vp, i64, ci, ctypes.c_float, vp, vp, vp]
         L.fp8_cast_f32.restype = ci
         L.fp8_cast_f32.argtypes = [vp, i64, ci, vp, vp]
         _lib = L
@@ -210,6 +214,37 @@ def fp8_kv_dequant(q: torch.Tensor, scales: torch.Tensor, out=None):
     rc = lib().fp8_kv_dequant(_p(q), T, D, q.stride(0), _p(scales), _p(out), out.stride(0), _stream(q))
     _check("fp8_kv_dequant", rc)
     return out
+
+
+class DelayedScaler:
+    """Per-tensor delayed scaling with an amax history (state in device
+    memory): quantize(x) uses the scale from earlier steps and returns
+    (codes uint8, scale_used float32 [1]); the state then holds the next
+    scale.  algo "max" (window maximum) or "latest"; divisor 400 by default."""
+
+    def __init__(self, history_len=16, algo="max", divisor=400.0, device="cuda"):
+        _need(algo in ("max", "latest"), "algo must be 'max' or 'latest'")
+        self.history_len = int(history_len)
+        self.algo = 0 if algo == "max" else 1
+        self.divisor = float(divisor)
+        nbytes = 16 + 4 * self.history_len
+        self.state = torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
+        self.reset()
+
+    def reset(self):
+        rc = lib().fp8_delayed_state_init(_p(self.state), self.history_len, _stream(self.state))
+        _check("fp8_delayed_state_init", rc)
+
+    def quantize(self, x: torch.Tensor, q=None, scale_used=None):
+        _need(x.dtype == torch.bfloat16 and x.is_contiguous(), "x must be contiguous bf16")
+        if q is None:
+            q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        if scale_used is None:
+            scale_used = torch.empty(1, dtype=torch.float32, device=x.device)
+        rc = lib().fp8_delayed_quant(_p(x), x.numel(), _p(self.state), self.history_len, self.algo,
+                                     self.divisor, _p(q), _p(scale_used), _stream(x))
+        _check("fp8_delayed_quant", rc)
+        return q, scale_used
 
 
 def fp8_block_gemm(a, a_scales, w, w_scales, out_dtype=torch.bfloat16, y=None):

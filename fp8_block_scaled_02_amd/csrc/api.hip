@@ -144,6 +144,25 @@ FP8B_EXPORT int fp8_kv_dequant(const uint8_t* q, int64_t T, int64_t D, int64_t l
   return fp8blk::launch_kv_dequant(q, T, D, ld_q, scales, out, ld_out, as_stream(stream));
 }
 
+FP8B_EXPORT int fp8_delayed_state_init(void* state, int64_t history_len, void* stream) {
+  if (!state) return FP8B_EINVAL;
+  if (history_len < 1 || history_len > FP8B_DELAYED_MAX_HISTORY) return FP8B_EINVAL;
+  if (!aligned(state, 16)) return FP8B_EALIGN;
+  return fp8blk::launch_delayed_init(state, history_len, as_stream(stream));
+}
+
+FP8B_EXPORT int fp8_delayed_quant(const void* x, int64_t n, void* state, int64_t history_len, int algo,
+                                  float amax_divisor, uint8_t* q, float* scale_used, void* stream) {
+  if (algo != FP8B_AMAX_MAX && algo != FP8B_AMAX_LATEST) return FP8B_EUNSUPPORTED;
+  if (!x || !state || !q || !scale_used) return FP8B_EINVAL;
+  if (n <= 0 || n % 8 != 0 || n / 8 / 1024 >= INT32_MAX) return FP8B_EINVAL;
+  if (history_len < 1 || history_len > FP8B_DELAYED_MAX_HISTORY) return FP8B_EINVAL;
+  if (!(amax_divisor > 0.0f) || amax_divisor > 3.0e38f) return FP8B_EINVAL;
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(state, 16) || !aligned(scale_used, 4)) return FP8B_EALIGN;
+  return fp8blk::launch_delayed_quant(x, n, state, history_len, algo, amax_divisor, q, scale_used,
+                                      as_stream(stream));
+}
+
 FP8B_EXPORT int fp8_cast_f32(const float* x, int64_t n, int fmt, uint8_t* q, void* stream) {
   if (fmt != FP8B_FMT_E4M3 && fmt != FP8B_FMT_E5M2) return FP8B_EUNSUPPORTED;
   if (!x || !q || n < 0) return FP8B_EINVAL;

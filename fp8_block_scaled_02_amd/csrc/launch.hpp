@@ -22,6 +22,9 @@ int launch_kv_dequant(const uint8_t* q, int64_t T, int64_t D, int64_t ldq, const
                       int64_t ldo, hipStream_t s);
 int launch_moe_combine(const void* y, int64_t R, int64_t N, const int32_t* token_rows, const float* gates,
                        int64_t T, int64_t topk, void* out, int out_bf16, hipStream_t s);
+int launch_delayed_init(void* state, int64_t L, hipStream_t s);
+int launch_delayed_quant(const void* x, int64_t n, void* state, int64_t L, int algo, float divisor, uint8_t* q,
+                         float* scale_used, hipStream_t s);
 int launch_weight_dequant(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, const float* scales,
                           void* w, int64_t ldw, hipStream_t s);
 int launch_block_gemm(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w,

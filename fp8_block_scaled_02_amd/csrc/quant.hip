@@ -10,6 +10,8 @@
 // (one 16-byte load), the lanes of one quantisation block are adjacent in a
 // wavefront, the block maximum is reduced with DPP inside the wave (no LDS,
 // no barrier), and each lane writes its 8 codes with one 8-byte store.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -284,6 +286,121 @@ __global__ __launch_bounds__(256) void kv_dequant_kernel(
   dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
+// Delayed scaling (ROCm 7.0 FP8/MXFP8/MXFP4 article, training part,
+// "Delayed Scaling": a step is quantised with the scale derived from
+// earlier steps, and the next scale is taken from the current amax with a
+// margin, amax / 400; its pitfall section adds an amax history window with
+// the "max" algorithm).  One scale per tensor.  The state lives in device
+// memory, laid out as fp8b_delayed_state (scale, running amax bits, next
+// history slot, filled count, then the history), so a step is two kernels
+// in stream order and never needs the host.
+struct DelayedHeader {
+  float scale;
+  uint32_t step_amax;
+  int32_t pos;
+  int32_t filled;
+};
+
+__global__ __launch_bounds__(256) void delayed_init_kernel(uint8_t* __restrict__ st, int L) {
+  DelayedHeader* h = reinterpret_cast<DelayedHeader*>(st);
+  float* hist = reinterpret_cast<float*>(st + sizeof(DelayedHeader));
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < L) hist[i] = 0.0f;
+  if (i == 0) {
+    h->scale = 1.0f;
+    h->step_amax = 0u;
+    h->pos = 0;
+    h->filled = 0;
+  }
+}
+
+// Step part 1: codes = E4M3(clamp(x / d, +-448)) with the stored scale d
+// (IEEE division: d comes from another tensor, so the quotient can take any
+// magnitude), and the running amax of this step via one atomic max per
+// workgroup (non-negative floats order like their bit patterns).
+constexpr int kDelayedUnroll = 4;
+constexpr int kDelayedMaxGroups = 1024;  // caps the atomics on the one amax word
+
+__global__ __launch_bounds__(256) void delayed_quant_kernel(
+    const uint16_t* __restrict__ x, int64_t n, const float* __restrict__ scale_in,
+    uint32_t* __restrict__ step_amax, uint8_t* __restrict__ q, float* __restrict__ scale_used) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const float d = *scale_in;
+  const int64_t nch = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * 256 * kDelayedUnroll;
+  float amax = 0.0f;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * kDelayedUnroll + tid; base < nch; base += stride) {
+    uint4 raw[kDelayedUnroll];
+#pragma unroll
+    for (int u = 0; u < kDelayedUnroll; ++u) {
+      const int64_t c = base + (int64_t)u * 256;
+      u32x4 v = {0, 0, 0, 0};
+      if (c < nch) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + 8 * c));
+      raw[u] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+#pragma unroll
+    for (int u = 0; u < kDelayedUnroll; ++u) {
+      const int64_t c = base + (int64_t)u * 256;
+      const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      if (c < nch) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = clamp448(f[i] / d);
+        uint2 out;
+        out.x = pack4_e4m3(v[0], v[1], v[2], v[3]);
+        out.y = pack4_e4m3(v[4], v[5], v[6], v[7]);
+        *reinterpret_cast<uint2*>(q + 8 * c) = out;
+      }
+    }
+  }
+  amax = row16_max(amax);
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  if (tid == 0) {
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    atomicMax(step_amax, __float_as_uint(amax));
+    if (blockIdx.x == 0) *scale_used = d;
+  }
+}
+
+// Step part 2 (one wave): push this step's amax into the history and set
+// the next scale = h / divisor (1 if h = 0), h = the window maximum (algo
+// 0) or this step's amax (algo 1); reset the running amax.
+__global__ __launch_bounds__(64) void delayed_update_kernel(uint8_t* __restrict__ st, int L, int algo,
+                                                            float divisor) {
+  DelayedHeader* hd = reinterpret_cast<DelayedHeader*>(st);
+  float* hist = reinterpret_cast<float*>(st + sizeof(DelayedHeader));
+  const int lane = threadIdx.x;
+  const float a = __uint_as_float(hd->step_amax);
+  const int pos = hd->pos;
+  const int filled = min(hd->filled + 1, L);
+  float h = a;
+  if (algo == 0) {
+    for (int i = lane; i < filled; i += 64) h = fmaxf(h, i == pos ? a : hist[i]);
+    h = row16_max(h);
+    h = fmaxf(h, __shfl_xor(h, 16));
+    h = fmaxf(h, __shfl_xor(h, 32));
+  }
+  if (lane == 0) {
+    hist[pos] = a;
+    hd->pos = (pos + 1) % L;
+    hd->filled = filled;
+    hd->scale = (h == 0.0f) ? 1.0f : h / divisor;
+    hd->step_amax = 0u;
+  }
+}
+
 // ---- host launchers --------------------------------------------------------
 constexpr int kActUnroll = 4;
 
@@ -348,6 +465,25 @@ int launch_kv_dequant(const uint8_t* q, int64_t T, int64_t D, int64_t ldq, const
   const dim3 grid((unsigned)((T * (D / 16) + 255) / 256));
   hipLaunchKernelGGL(kv_dequant_kernel, grid, dim3(256), 0, s, q, T, D, ldq, scales, static_cast<uint16_t*>(out),
                      ldo);
+  return check_launch();
+}
+
+int launch_delayed_init(void* state, int64_t L, hipStream_t s) {
+  hipLaunchKernelGGL(delayed_init_kernel, dim3((unsigned)((L + 255) / 256)), dim3(256), 0, s,
+                     static_cast<uint8_t*>(state), (int)L);
+  return check_launch();
+}
+
+int launch_delayed_quant(const void* x, int64_t n, void* state, int64_t L, int algo, float divisor, uint8_t* q,
+                         float* scale_used, hipStream_t s) {
+  uint8_t* st = static_cast<uint8_t*>(state);
+  DelayedHeader* h = reinterpret_cast<DelayedHeader*>(st);
+  const int64_t per_wg = 256 * kDelayedUnroll;
+  const dim3 grid((unsigned)std::min<int64_t>((n / 8 + per_wg - 1) / per_wg, kDelayedMaxGroups));
+  hipLaunchKernelGGL(delayed_quant_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(x), n, &h->scale,
+                     &h->step_amax, q, scale_used);
+  if (check_launch() != FP8B_OK) return FP8B_ELAUNCH;
+  hipLaunchKernelGGL(delayed_update_kernel, dim3(1), dim3(64), 0, s, st, (int)L, algo, divisor);
   return check_launch();
 }
 

@@ -261,6 +261,52 @@ int fp8_kv_dequant(const uint8_t *q, int64_t T, int64_t D, int64_t ld_q,
                    void *stream);
 
 /*
+ * Delayed scaling (ROCm 7.0 FP8/MXFP8/MXFP4 article, training part,
+ * "Delayed Scaling": quantise a step with the scale derived from earlier
+ * steps, then take the next scale from the current amax with a safety
+ * margin, amax / 400, starting from scale 1; its pitfall section: an amax
+ * history window (amax_history_len) and the "max" compute algorithm).
+ * One scale per tensor.  The state is device memory owned by the caller:
+ *
+ *   fp8b_delayed_state header (16 bytes) followed by float history[len].
+ *
+ * fp8_delayed_state_init writes the initial state (scale 1, empty history)
+ * with a kernel (no memset, so it may be captured in a graph).
+ *
+ * fp8_delayed_quant runs one step on the stream:
+ *   d = state.scale;  q[i] = E4M3(clamp(fp32(x[i] / d), -448, 448));
+ *   *scale_used = d (the dequantisation scale of these codes);
+ *   amax = max_i |x[i]| pushed into the history (the oldest entry leaves
+ *   once `history_len` are held);
+ *   state.scale = fp32(h / amax_divisor), or 1 if h = 0, where h is the
+ *   history maximum (FP8B_AMAX_MAX) or this step's amax (FP8B_AMAX_LATEST).
+ *   Calls that share a state must be ordered (one stream); the same
+ *   history_len must be passed to every call on a state.
+ *
+ *   x            bf16 [n], 16-byte aligned; n > 0, n % 8 == 0.
+ *   state        FP8B_DELAYED_STATE_BYTES(history_len) bytes, 16-byte
+ *                aligned; 1 <= history_len <= FP8B_DELAYED_MAX_HISTORY.
+ *   amax_divisor > 0 (the article uses 400: 448 with about 10% margin).
+ *   q            uint8 codes [n], 8-byte aligned.
+ *   scale_used   float [1].
+ */
+#define FP8B_DELAYED_MAX_HISTORY 65536
+#define FP8B_DELAYED_STATE_BYTES(len) (16 + 4 * (int64_t)(len))
+typedef struct {
+  float scale;        /* the scale the next step uses                   */
+  uint32_t step_amax; /* running amax of a step in flight (float bits)  */
+  int32_t pos;        /* next history slot                              */
+  int32_t filled;     /* history entries written so far (<= len)       */
+  /* float history[len] follows */
+} fp8b_delayed_state;
+typedef enum { FP8B_AMAX_MAX = 0, FP8B_AMAX_LATEST = 1 } fp8b_amax_algo;
+
+int fp8_delayed_state_init(void *state, int64_t history_len, void *stream);
+int fp8_delayed_quant(const void *x, int64_t n, void *state,
+                      int64_t history_len, int algo, float amax_divisor,
+                      uint8_t *q, float *scale_used, void *stream);
+
+/*
  * fp8_cast_f32 -- FP8Cast of "量化: FP8 与混合精度推理" (x_fp8 =
  * FP8Cast(x / s)) with s = 1: clamp each fp32 value to +-Fmax (448 for
  * E4M3, 57344 for E5M2) and round to nearest, ties to even.

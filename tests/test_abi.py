@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
     assert _declared() == sorted([
         "fp8b_abi_version", "fp8b_status_string", "fp8_act_quant", "fp8_weight_quant",
         "fp8_block_gemm", "mxfp8_gemm", "fp8_grouped_gemm", "fp8_moe_combine", "fp8_weight_dequant", "fp8_kv_quant", "fp8_kv_dequant",
-        "fp8_cast_f32"])
+        "fp8_delayed_state_init", "fp8_delayed_quant", "fp8_cast_f32"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -99,6 +99,23 @@ def test_moe_combine_validation(L):
     assert f(*bad) == -2
     bad = list(args); bad[5] = 0
     assert f(*bad) == 0                                                   # T = 0
+
+
+def test_delayed_validation(L):
+    f = L.fp8_delayed_quant
+    args = [GOOD, 1024, GOOD, 16, 0, 400.0, GOOD, GOOD, NULL]
+    bad = list(args); bad[4] = 2
+    assert f(*bad) == -3
+    bad = list(args); bad[1] = 100
+    assert f(*bad) == -1                                                  # n % 8
+    bad = list(args); bad[3] = 0
+    assert f(*bad) == -1                                                  # history_len
+    bad = list(args); bad[5] = 0.0
+    assert f(*bad) == -1                                                  # divisor
+    bad = list(args); bad[0] = ODD
+    assert f(*bad) == -2
+    assert L.fp8_delayed_state_init(NULL, 16, NULL) == -1
+    assert L.fp8_delayed_state_init(GOOD, 0, NULL) == -1
 
 
 def test_kv_validation(L):

@@ -293,3 +293,45 @@ def test_kv_dequant_every_code_and_strides(F, orc):
     o = _np(out.view(torch.int16)).view(np.uint16)
     assert (o[:, 512:] == 0xFFFF).all()
     _deq_check(o[:, :512], orc.kv_dequant(q, s), "kv dequant codes")
+
+
+# ---- delayed scaling ----------------------------------------------------------
+def _delayed_steps(S, n, seed, dev="cpu"):
+    g = W.gen(seed, dev)
+    mag = torch.exp2(torch.rand(S, 1, generator=g, device=dev) * 12 - 6)
+    x = (torch.randn(S, n, generator=g, device=dev) * mag).to(torch.bfloat16)
+    x[S // 2] = 0                                        # an all-zero step
+    return x
+
+
+@pytest.mark.parametrize("L,algo", [(3, "max"), (1, "max"), (16, "latest"), (64, "max")])
+def test_delayed_scaling_steps(F, orc, L, algo):
+    S, n = 10, 64 * 7168
+    x = _delayed_steps(S, n, L)
+    ds = F.DelayedScaler(L, algo, 400.0)
+    xd = x.to(DEV)
+    got_q, got_s = [], []
+    for s in range(S):
+        q, su = ds.quantize(xd[s])
+        got_q.append(_np(q)), got_s.append(_np(su)[0])
+    q2, s2 = orc.delayed_scaling(W.bits(x), L, 0 if algo == "max" else 1, 400.0)
+    np.testing.assert_array_equal(np.array(got_s, np.float32).view(np.uint32), s2.view(np.uint32))
+    for s in range(S):
+        bad = np.flatnonzero(got_q[s] != q2[s])
+        assert len(bad) == 0, f"step {s}: {len(bad)} code mismatches, first {bad[0]}"
+    # reset restarts the sequence
+    ds.reset()
+    q, su = ds.quantize(xd[0])
+    assert _np(su)[0] == 1.0 and (_np(q) == q2[0]).all()
+
+
+def test_delayed_scaling_full_activation(F, orc):
+    S, n = 3, 4096 * 7168
+    x = _delayed_steps(S, n, 99, DEV)
+    ds = F.DelayedScaler(16, "max", 400.0)
+    outs = [ds.quantize(x[s]) for s in range(S)]
+    torch.cuda.synchronize()
+    q2, s2 = orc.delayed_scaling(W.bits(x), 16, 0, 400.0)
+    for s, (q, su) in enumerate(outs):
+        assert _np(su)[0] == s2[s], s
+        assert (_np(q) == q2[s]).all(), s
