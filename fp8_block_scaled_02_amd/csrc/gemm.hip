@@ -233,27 +233,39 @@ __device__ __forceinline__ Frag16 widen(const Raw16& v, float s_lo, float s_hi) 
 // widens a quarter of fragment j+1 and folds fragment j-1's product for
 // subtile row k into acc (acc += P * sa * sw); those have long been
 // complete, so no VALU op waits on an MFMA in flight.
-template <class C>
-__device__ __forceinline__ void compute_block(const uint8_t* buf, v4f (&acc)[C::MI][C::NJ]) {
+template <class C, class Hook>
+__device__ __forceinline__ void compute_block(const uint8_t* buf, v4f (&acc)[C::MI][C::NJ], Hook hook) {
   static_assert(C::MI == 4, "one rescale row per K sub-step window");
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave % C::WM, wn = wave / C::WM, l16 = lane & 15, g = lane >> 4;
   const float* sa = reinterpret_cast<const float*>(buf + C::OFF_SA);
   const float* sw = reinterpret_cast<const float*>(buf + C::OFF_SB);
   const uint8_t* wt = buf + C::OFF_W;
+  // LDS reads: the scales, the four A fragments and the first two weight
+  // fragments go out together (15 reads, the most the LDS wait counter can
+  // track), later weight fragments two subtiles ahead of their use inside
+  // the MFMA loop.
   Raw16 wraw[C::NJ];
-#pragma unroll
-  for (int j = 0; j < C::NJ; ++j) wraw[j] = read_raw(wt, wn * C::TN + 16 * j + l16, g);
   Frag16 xf[C::MI];
   float s[C::MI];
+  float sar[C::MI];
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i) sar[i] = sa[wm * C::TM + 16 * i + l16];
   const float sw0 = sw[(wn * C::TN) / 128];
+  Raw16 araw[C::MI];
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i) araw[i] = read_raw(buf, wm * C::TM + 16 * i + l16, g);
+#pragma unroll
+  for (int j = 0; j < 2 && j < C::NJ; ++j) wraw[j] = read_raw(wt, wn * C::TN + 16 * j + l16, g);
 #pragma unroll
   for (int i = 0; i < C::MI; ++i) {
-    const int r = wm * C::TM + 16 * i + l16;
-    xf[i] = widen(read_raw(buf, r, g), 1.0f, 1.0f);
-    s[i] = sa[r] * sw0;
+    xf[i] = widen(araw[i], 1.0f, 1.0f);
+    s[i] = sar[i] * sw0;
   }
   Frag16 wcur = widen(wraw[0], 1.0f, 1.0f), wnext;
+  // the next stage's direct-to-LDS loads (see k_step); the compiler places
+  // them right behind the first reads, which measured best for this loop
+  hook();
   v4f p[C::MI], prev[C::MI];
 #if FP8B_SCHED == 2
   __builtin_amdgcn_iglp_opt(0);
@@ -262,6 +274,7 @@ __device__ __forceinline__ void compute_block(const uint8_t* buf, v4f (&acc)[C::
 #endif
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j) {
+    if (j + 2 < C::NJ) wraw[j + 2] = read_raw(wt, wn * C::TN + 16 * (j + 2) + l16, g);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
 #if FP8B_SCHED == 1
@@ -313,26 +326,45 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
 // in bf16's normal range), so the MFMAs accumulate straight into acc.  The
 // lane's first 16 codes (K 16g..) lie in 32-block g/2 and its last 16
 // (K 64+16g..) in 32-block 2 + g/2; scale bytes are one dword per row.
-template <class C>
-__device__ __forceinline__ void compute_mx(const uint8_t* buf, v4f (&acc)[C::MI][C::NJ]) {
+template <class C, class Hook>
+__device__ __forceinline__ void compute_mx(const uint8_t* buf, v4f (&acc)[C::MI][C::NJ], Hook hook) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave % C::WM, wn = wave / C::WM, l16 = lane & 15, g = lane >> 4;
   const uint32_t* ea = reinterpret_cast<const uint32_t*>(buf + C::OFF_SA);
   const uint32_t* eb = reinterpret_cast<const uint32_t*>(buf + C::OFF_SB);
   const int b0 = 8 * (g >> 1), b1 = 8 * (2 + (g >> 1));
-  Frag16 xf[C::MI];
+  // reads first (A fragments, their scales, the first weight fragment),
+  // then the conversions; later weight fragments one subtile ahead
+  Raw16 araw[C::MI], wraw[2];
+  uint32_t eav[C::MI], ebv[2];
 #pragma unroll
   for (int i = 0; i < C::MI; ++i) {
     const int r = wm * C::TM + 16 * i + l16;
-    const uint32_t e = ea[r];
-    xf[i] = widen(read_raw(buf, r, g), e8m0_to_f32((e >> b0) & 0xffu), e8m0_to_f32((e >> b1) & 0xffu));
+    eav[i] = ea[r];
+    araw[i] = read_raw(buf, r, g);
   }
+  ebv[0] = eb[wn * C::TN + l16];
+  wraw[0] = read_raw(buf + C::OFF_W, wn * C::TN + l16, g);
+  Frag16 xf[C::MI];
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+    xf[i] = widen(araw[i], e8m0_to_f32((eav[i] >> b0) & 0xffu), e8m0_to_f32((eav[i] >> b1) & 0xffu));
+  // the conversions above are pinned before the next stage's direct-to-LDS
+  // loads (see k_step), so their LDS waits stay exact (9% faster at 8192^3
+  // than letting the compiler hoist the loads)
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+    asm volatile("" : "+v"(xf[i].k[0]), "+v"(xf[i].k[1]), "+v"(xf[i].k[2]), "+v"(xf[i].k[3])::"memory");
+  hook();
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j) {
-    const int r = wn * C::TN + 16 * j + l16;
-    const uint32_t e = eb[r];
-    const Frag16 wf = widen(read_raw(buf + C::OFF_W, r, g), e8m0_to_f32((e >> b0) & 0xffu),
-                            e8m0_to_f32((e >> b1) & 0xffu));
+    if (j + 1 < C::NJ) {
+      const int rn = wn * C::TN + 16 * (j + 1) + l16;
+      ebv[(j + 1) & 1] = eb[rn];
+      wraw[(j + 1) & 1] = read_raw(buf + C::OFF_W, rn, g);
+    }
+    const uint32_t e = ebv[j & 1];
+    const Frag16 wf = widen(wraw[j & 1], e8m0_to_f32((e >> b0) & 0xffu), e8m0_to_f32((e >> b1) & 0xffu));
     // k-outer order: consecutive MFMAs go to different accumulators
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -346,14 +378,24 @@ __device__ __forceinline__ void compute_mx(const uint8_t* buf, v4f (&acc)[C::MI]
 // being read).  Step kb: wait for this wave's loads of step kb (the loads of
 // the S-2 later steps may stay in flight), one barrier (everyone's loads of
 // step kb are visible and everyone is done reading the stage about to be
-// refilled), issue step kb+S-1, compute step kb.
+// refilled), compute step kb, and issue step kb+S-1 from inside it, once
+// the step's first LDS reads have been consumed.  (While a direct-to-LDS
+// load is in flight the compiler can only wait for all outstanding LDS
+// reads at once, so issuing the loads first would expose the full LDS
+// latency before every fragment; issued after the first batch of reads,
+// the later full waits only cover reads that have long landed.)
 template <class C>
 __device__ __forceinline__ void k_step(uint8_t* cur, uint8_t* refill, const Src<C>& src, int kb, int nkb,
                                        v4f (&acc)[C::MI][C::NJ]) {
   if (C::S == 3 && kb + 1 < nkb) wait_vmem<C::NI>(); else wait_vmem<0>();
   __syncthreads();
-  if (kb + C::S - 1 < nkb) issue<C>(refill, src, kb + C::S - 1);
-  if (C::MX) compute_mx<C>(cur, acc); else compute_block<C>(cur, acc);
+  auto hook = [&]() {
+    if (kb + C::S - 1 < nkb) issue<C>(refill, src, kb + C::S - 1);
+  };
+  if constexpr (C::MX)
+    compute_mx<C>(cur, acc, hook);
+  else
+    compute_block<C>(cur, acc, hook);
 }
 
 template <class C>
