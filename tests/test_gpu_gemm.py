@@ -61,7 +61,8 @@ def test_block_gemm_ragged(F, orc, M, N, K, out):
     assert_parity(yg, yr, bnd, out == torch.bfloat16, f"{M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 512, 1152), (7, 384, 640), (16, 128, 128), (17, 256, 384),
+@pytest.mark.parametrize("M,N,K", [(1, 512, 1152), (2, 256, 640), (1, 128, 128), (2, 384, 2176),
+                                   (7, 384, 640), (16, 128, 128), (17, 256, 384),
                                    (20, 256, 1152), (32, 640, 2048)])
 def test_block_gemm_few_tokens(F, orc, M, N, K):
     """M <= 32 takes the streaming decode kernel: one and two 16-token
