@@ -174,3 +174,17 @@ def test_binding_rejects_cpu_misuse():
     import fp8_block_scaled_02_amd as F
     with pytest.raises(ValueError):
         F.fp8_act_quant(torch.zeros(4, 128, dtype=torch.float32))
+
+
+def test_header_compiles_as_c99(tmp_path):
+    """The boundary header is plain C: it compiles warning-free as C99 and
+    its state-size macro and enums are usable from C."""
+    import subprocess
+    src = tmp_path / "use.c"
+    src.write_text('#include "fp8blk.h"\n'
+                   'int main(void) { fp8b_delayed_state s; (void)s;\n'
+                   '  return (int)FP8B_DELAYED_STATE_BYTES(4) + FP8B_AMAX_MAX + FP8B_OK + FP8B_SCALE_FP32; }\n')
+    inc = os.path.join(os.path.dirname(__file__), "..", "include")
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", inc, "-c",
+                        str(src), "-o", str(tmp_path / "use.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
