@@ -14,6 +14,8 @@
 
 namespace fp8blk {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void moe_combine_kernel(
     const uint16_t* __restrict__ y, int64_t R, int64_t N, const int32_t* __restrict__ token_rows,
@@ -57,7 +59,8 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(
     o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
     o.z = f32_to_bf16_bits(acc[4]) | (f32_to_bf16_bits(acc[5]) << 16);
     o.w = f32_to_bf16_bits(acc[6]) | (f32_to_bf16_bits(acc[7]) << 16);
-    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + t * N + n) = o;
+    __builtin_nontemporal_store(u32x4{o.x, o.y, o.z, o.w},
+                                reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + t * N + n));
   } else {
     float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + t * N + n);
     o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);

@@ -9,7 +9,8 @@
 // the kernel is built for streaming: every lane owns 8 consecutive bf16
 // (one 16-byte load), the lanes of one quantisation block are adjacent in a
 // wavefront, the block maximum is reduced with DPP inside the wave (no LDS,
-// no barrier), and each lane writes its 8 codes with one 8-byte store.
+// no barrier), and each lane writes its 8 codes with one 8-byte
+// non-temporal store.
 #include <algorithm>
 
 #include "common.hpp"
@@ -18,35 +19,36 @@
 namespace fp8blk {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // FMT: 0 fp32 scales, 1 power-of-two scales stored as fp32, 2 E8M0 bytes.
-// Each thread owns UNROLL 16-byte chunks, 256 chunks apart, all loaded
-// before any is processed (bytes in flight per lane = 16 * UNROLL).
+// Grid: x = token row, y = segment of 256 * UNROLL 16-byte chunks of the
+// row (so no index needs a division); each thread owns UNROLL chunks 256
+// apart, all loaded before any is processed (bytes in flight per lane =
+// 16 * UNROLL).
 template <int BLOCK, int FMT, int UNROLL>
 __global__ __launch_bounds__(256) void act_quant_kernel(
-    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+    const uint16_t* __restrict__ x, int64_t K, int64_t ldx,
     uint8_t* __restrict__ q, int64_t ldq, void* __restrict__ scales) {
   constexpr int LPB = BLOCK / 8;  // lanes per quantisation block
-  const int64_t cpr = K / 8;      // 16-byte chunks per row
-  const int64_t total = M * cpr;
-  const int64_t nblk = K / BLOCK;
-  const int64_t base = ((int64_t)blockIdx.x * 256 * UNROLL) + threadIdx.x;
+  const int cpr = (int)(K / 8);   // 16-byte chunks per row
+  const int nblk = (int)(K / BLOCK);
+  const int64_t row = blockIdx.x;
+  const int base = (int)blockIdx.y * 256 * UNROLL + (int)threadIdx.x;
+  const uint16_t* xr = x + row * ldx;
+  uint8_t* qr = q + row * ldq;
 
   uint4 raw[UNROLL];
-  int64_t row[UNROLL], col[UNROLL];
-  bool ok[UNROLL];
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
-    const int64_t c = base + (int64_t)u * 256;
-    ok[u] = c < total;
-    row[u] = ok[u] ? c / cpr : 0;
-    col[u] = ok[u] ? (c - row[u] * cpr) * 8 : 0;
+    const int c = base + u * 256;
     u32x4 v = {0, 0, 0, 0};
-    if (ok[u]) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + row[u] * ldx + col[u]));
+    if (c < cpr) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + 8 * c));
     raw[u] = make_uint4(v[0], v[1], v[2], v[3]);
   }
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
+    const int c = base + u * 256;
     float f[8];
     const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
 #pragma unroll
@@ -60,8 +62,9 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
     amax = (LPB == 16) ? row16_max(amax) : quad_max(amax);
 
     float qv[8];
-    const bool lead = ok[u] && (col[u] % BLOCK) == 0;
-    const int64_t sidx = row[u] * nblk + col[u] / BLOCK;
+    const bool ok = c < cpr;
+    const bool lead = ok && (c % LPB) == 0;
+    const int64_t sidx = row * nblk + c / LPB;
     if (FMT == 0) {
       const float d = (amax == 0.0f) ? 1.0f : amax / 448.0f;  // IEEE division
       const BlockDivisor bd = make_divisor(amax, d);
@@ -81,11 +84,13 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
           reinterpret_cast<uint8_t*>(scales)[sidx] = (uint8_t)(127 + e);
       }
     }
-    if (ok[u]) {
-      uint2 out;
-      out.x = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
-      out.y = pack4_e4m3(qv[4], qv[5], qv[6], qv[7]);
-      *reinterpret_cast<uint2*>(q + row[u] * ldq + col[u]) = out;
+    if (ok) {
+      u32x2 out;
+      out[0] = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
+      out[1] = pack4_e4m3(qv[4], qv[5], qv[6], qv[7]);
+      // codes are written once and read by a later kernel: non-temporal
+      // (measured 13-18% faster than a plain store)
+      __builtin_nontemporal_store(out, reinterpret_cast<u32x2*>(qr + 8 * c));
     }
   }
 }
@@ -200,9 +205,9 @@ __global__ __launch_bounds__(256) void weight_dequant_kernel(
     out[2 * i] = f32_to_bf16_bits(lo[0] * d) | (f32_to_bf16_bits(lo[1] * d) << 16);
     out[2 * i + 1] = f32_to_bf16_bits(hi[0] * d) | (f32_to_bf16_bits(hi[1] * d) << 16);
   }
-  uint4* dst = reinterpret_cast<uint4*>(w + n * ldw + k);
-  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  u32x4* dst = reinterpret_cast<u32x4*>(w + n * ldw + k);
+  __builtin_nontemporal_store(u32x4{out[0], out[1], out[2], out[3]}, dst);
+  __builtin_nontemporal_store(u32x4{out[4], out[5], out[6], out[7]}, dst + 1);
 }
 
 // KV-cache quantisation ("LLM 推理的 FP8 混合精度工程 2026", section 4: the
@@ -254,10 +259,10 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(
       v[2 * i] = fminf(fmaxf(divide(bf16_bits_to_f32(w[i] & 0xffffu), bd), -57344.0f), 57344.0f);
       v[2 * i + 1] = fminf(fmaxf(divide(__uint_as_float(w[i] & 0xffff0000u), bd), -57344.0f), 57344.0f);
     }
-    uint2 out;
-    out.x = pack4_e5m2(v[0], v[1], v[2], v[3]);
-    out.y = pack4_e5m2(v[4], v[5], v[6], v[7]);
-    *reinterpret_cast<uint2*>(q + t * ldq + 8 * c) = out;
+    u32x2 out;
+    out[0] = pack4_e5m2(v[0], v[1], v[2], v[3]);
+    out[1] = pack4_e5m2(v[4], v[5], v[6], v[7]);
+    __builtin_nontemporal_store(out, reinterpret_cast<u32x2*>(q + t * ldq + 8 * c));
   }
 }
 
@@ -281,9 +286,9 @@ __global__ __launch_bounds__(256) void kv_dequant_kernel(
     o[2 * i] = f32_to_bf16_bits(lo[0] * d) | (f32_to_bf16_bits(lo[1] * d) << 16);
     o[2 * i + 1] = f32_to_bf16_bits(hi[0] * d) | (f32_to_bf16_bits(hi[1] * d) << 16);
   }
-  uint4* dst = reinterpret_cast<uint4*>(out + t * ldo + k);
-  dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-  dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  u32x4* dst = reinterpret_cast<u32x4*>(out + t * ldo + k);
+  __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, dst);
+  __builtin_nontemporal_store(u32x4{o[4], o[5], o[6], o[7]}, dst + 1);
 }
 
 // Delayed scaling (ROCm 7.0 FP8/MXFP8/MXFP4 article, training part,
@@ -355,10 +360,10 @@ __global__ __launch_bounds__(256) void delayed_quant_kernel(
         float v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = clamp448(f[i] / d);
-        uint2 out;
-        out.x = pack4_e4m3(v[0], v[1], v[2], v[3]);
-        out.y = pack4_e4m3(v[4], v[5], v[6], v[7]);
-        *reinterpret_cast<uint2*>(q + 8 * c) = out;
+        u32x2 out;
+        out[0] = pack4_e4m3(v[0], v[1], v[2], v[3]);
+        out[1] = pack4_e4m3(v[4], v[5], v[6], v[7]);
+        __builtin_nontemporal_store(out, reinterpret_cast<u32x2*>(q + 8 * c));
       }
     }
   }
@@ -402,16 +407,19 @@ __global__ __launch_bounds__(64) void delayed_update_kernel(uint8_t* __restrict_
 }
 
 // ---- host launchers --------------------------------------------------------
+// 4 chunks per lane: a 7168- or 8192-wide row is one segment of 1024
+// chunks (2 and 8 measured slower on 4096 x 7168).
 constexpr int kActUnroll = 4;
 
 int launch_act_quant(const void* x, int64_t M, int64_t K, int64_t ldx, int block, int fmt,
                      uint8_t* q, int64_t ldq, void* scales, hipStream_t s) {
-  const int64_t total = M * (K / 8);
-  const int64_t per_wg = 256 * kActUnroll;
-  const dim3 grid((unsigned)((total + per_wg - 1) / per_wg));
+  const int64_t cpr = K / 8;
+  const int64_t segs = (cpr + 256 * kActUnroll - 1) / (256 * kActUnroll);
+  if (segs > 65535 || M > 0x7fffffff) return FP8B_EINVAL;  // grid limits
+  const dim3 grid((unsigned)M, (unsigned)segs);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
 #define FP8B_AQ(B, F) \
-  hipLaunchKernelGGL((act_quant_kernel<B, F, kActUnroll>), grid, dim3(256), 0, s, xp, M, K, ldx, q, ldq, scales)
+  hipLaunchKernelGGL((act_quant_kernel<B, F, kActUnroll>), grid, dim3(256), 0, s, xp, K, ldx, q, ldq, scales)
   if (block == 128) {
     if (fmt == 0) FP8B_AQ(128, 0);
     else if (fmt == 1) FP8B_AQ(128, 1);
