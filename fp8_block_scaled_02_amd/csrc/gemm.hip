@@ -46,9 +46,6 @@
 
 namespace fp8blk {
 
-#ifndef FP8B_SCHED
-#define FP8B_SCHED 4  // 0: compiler, 1: sched_barrier windows, 2/3: iglp_opt, 4: register ties
-#endif
 
 constexpr int kBK = 128;
 constexpr int kGroupM = 8;  // m-tiles per tile-order group
@@ -227,9 +224,9 @@ __device__ __forceinline__ Frag16 widen(const Raw16& v, float s_lo, float s_hi) 
 
 // One K step of the block-scaled GEMM on the wave's MI x NJ subtiles.
 // For each weight fragment j the MI block products run as MI chains of four
-// bf16 MFMAs.  Scheduling windows (sched_barrier) pin the order k-outer /
-// i-inner, so consecutive MFMAs are independent: a dependent MFMA issued
-// right behind its producer stalls on gfx950.  Inside window k the VALU
+// bf16 MFMAs in k-outer / i-inner order, so consecutive MFMAs are
+// independent: a dependent MFMA issued right behind its producer stalls on
+// gfx950.  Inside window k (register ties keep the windows apart) the VALU
 // widens a quarter of fragment j+1 and folds fragment j-1's product for
 // subtile row k into acc (acc += P * sa * sw); those have long been
 // complete, so no VALU op waits on an MFMA in flight.
@@ -267,19 +264,11 @@ __device__ __forceinline__ void compute_block(const uint8_t* buf, v4f (&acc)[C::
   // them right behind the first reads, which measured best for this loop
   hook();
   v4f p[C::MI], prev[C::MI];
-#if FP8B_SCHED == 2
-  __builtin_amdgcn_iglp_opt(0);
-#elif FP8B_SCHED == 3
-  __builtin_amdgcn_iglp_opt(1);
-#endif
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j) {
     if (j + 2 < C::NJ) wraw[j + 2] = read_raw(wt, wn * C::TN + 16 * (j + 2) + l16, g);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-#if FP8B_SCHED == 1
-      __builtin_amdgcn_sched_barrier(0);
-#endif
 #pragma unroll
       for (int i = 0; i < C::MI; ++i)
         p[i] = mfma_bf16(wcur.k[k], xf[i].k[k], k == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : p[i]);
@@ -291,19 +280,15 @@ __device__ __forceinline__ void compute_block(const uint8_t* buf, v4f (&acc)[C::
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[k][j - 1][r] = __builtin_fmaf(prev[k][r], s[k], acc[k][j - 1][r]);
       }
-#if FP8B_SCHED == 4
       // order: this window's VALU results exist before the next window's
-      // MFMAs read their operands
+      // MFMAs read their operands (empty asm statements tie the registers;
+      // measured ahead of sched_barrier windows and iglp_opt)
       if (k < 3) {
         if (j > 0) asm volatile("" : "+v"(wcur.k[k + 1]), "+v"(acc[k][j - 1]));
         if (j + 1 < C::NJ) asm volatile("" : "+v"(wcur.k[k + 1]), "+v"(wnext.k[k]));
         asm volatile("" : "+v"(wcur.k[k + 1]), "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]));
       }
-#endif
     }
-#if FP8B_SCHED == 1
-    __builtin_amdgcn_sched_barrier(0);
-#endif
 #pragma unroll
     for (int i = 0; i < C::MI; ++i) prev[i] = p[i];
     if (j + 1 < C::NJ) wcur = wnext;
