@@ -332,3 +332,13 @@ def test_moe_forward_full(F, orc):
     yr, bnd = orc.grouped_gemm(oa_full, osa_full, case.row_index.numpy(), offs, wl, sl, rows=np.asarray(rows))
     assert_parity(_np(y[torch.as_tensor(rows, device=DEV)]), yr, bnd, True, "moe routed rows")
     print(f"moe combine worst {worst:.3g}")
+
+
+def test_grouped_max_experts(F, orc):
+    """1024 experts (the entry point's maximum), almost all empty: one large
+    expert, a few short ones, the rest with no rows."""
+    counts = [0] * 1024
+    counts[0], counts[511], counts[512], counts[1023] = 5, 300, 17, 1
+    case = _moe_counts_case(counts, T=96, N=128, K=256, seed=46)
+    yg, yr, bnd = _moe_run(F, orc, case)
+    assert_parity(yg, yr, bnd, True, "moe 1024 experts")

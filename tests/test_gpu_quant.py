@@ -335,3 +335,36 @@ def test_delayed_scaling_full_activation(F, orc):
     for s, (q, su) in enumerate(outs):
         assert _np(su)[0] == s2[s], s
         assert (_np(q) == q2[s]).all(), s
+
+
+def test_act_quant_non_finite_blocks_stay_local(F, orc):
+    """NaN and +-Inf inside some blocks: those blocks' codes and scales are
+    unspecified, but every other block must still match the oracle exactly
+    (and nothing faults)."""
+    g = W.gen(44)
+    x = W.activations(64, 1024, 4, 20.0, g)
+    xf = x.float()
+    xf[3, 5] = float("nan")
+    xf[10, 300] = float("inf")
+    xf[20, 1023] = float("-inf")
+    x = xf.to(torch.bfloat16)
+    bad_blocks = {(3, 0), (10, 2), (20, 7)}
+    for fmt, fi in (("fp32", 0), ("ue8m0", 1)):
+        q, s = F.fp8_act_quant(x.to(DEV), 128, fmt)
+        torch.cuda.synchronize()
+        q2, s2 = orc.act_quant(W.bits(x), 128, fi)
+        qn, sn = _np(q), _np(s)
+        for r in range(64):
+            for b in range(8):
+                if (r, b) in bad_blocks:
+                    continue
+                assert (qn[r, 128 * b:128 * (b + 1)] == q2[r, 128 * b:128 * (b + 1)]).all(), (fmt, r, b)
+                assert sn[r, b].view(np.uint32) == s2[r, b].view(np.uint32), (fmt, r, b)
+
+
+def test_act_quant_many_short_rows(F, orc):
+    """70000 token rows of 128 channels: the row grid dimension far beyond
+    65535 (the y-dimension limit)."""
+    g = W.gen(45)
+    x = W.activations(70000, 128, 1, 30.0, g)
+    _assert_same(*_run_act(F, orc, x, 128, "fp32"), "70000x128")
