@@ -11,6 +11,7 @@ namespace {
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every 32-bit tile index in range
+constexpr int64_t kMaxLd = (int64_t)1 << 24;   // GEMM leading dimensions: 32-bit offsets inside a tile
 
 }  // namespace
 
@@ -64,6 +65,7 @@ FP8B_EXPORT int fp8_block_gemm(const uint8_t* a, int64_t ld_a, const float* a_sc
   if (!a || !a_scales || !w || !w_scales || !y) return FP8B_EINVAL;
   if (M < 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8B_EINVAL;
   if (N % 128 != 0 || K % 128 != 0 || ld_a < K || ld_w < K || ld_y < N) return FP8B_EINVAL;
+  if (ld_a >= kMaxLd || ld_w >= kMaxLd) return FP8B_EINVAL;
   if (!aligned(a, 16) || !aligned(w, 16) || ld_a % 16 != 0 || ld_w % 16 != 0) return FP8B_EALIGN;
   if (!aligned(a_scales, 4) || !aligned(w_scales, 4) || !aligned(y, 16) || ld_y % 8 != 0) return FP8B_EALIGN;
   if (((M + 127) / 128) * (N / 128) >= INT32_MAX) return FP8B_EINVAL;
@@ -77,6 +79,7 @@ FP8B_EXPORT int mxfp8_gemm(const uint8_t* a, int64_t ld_a, const uint8_t* a_e8m0
   if (!a || !a_e8m0 || !b || !b_e8m0 || !y) return FP8B_EINVAL;
   if (M < 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8B_EINVAL;
   if (N % 128 != 0 || K % 128 != 0 || ld_a < K || ld_b < K || ld_y < N) return FP8B_EINVAL;
+  if (ld_a >= kMaxLd || ld_b >= kMaxLd) return FP8B_EINVAL;
   if (!aligned(a, 16) || !aligned(b, 16) || ld_a % 16 != 0 || ld_b % 16 != 0) return FP8B_EALIGN;
   if (!aligned(a_e8m0, 4) || !aligned(b_e8m0, 4) || !aligned(y, 16) || ld_y % 4 != 0) return FP8B_EALIGN;
   if (((M + 127) / 128) * (N / 128) >= INT32_MAX) return FP8B_EINVAL;
@@ -92,6 +95,12 @@ FP8B_EXPORT int fp8_grouped_gemm(const uint8_t* a, const float* a_scales, int64_
   if (T < 1 || R < 0 || E < 1 || E > 1024 || N <= 0 || K <= 0) return FP8B_EINVAL;
   if (T > kMaxDim || R > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8B_EINVAL;
   if (N % 128 != 0 || K % 128 != 0) return FP8B_EINVAL;
+  // the in-kernel work map counts tile items (128 x 128) and stream items
+  // (64 weight rows) in 32-bit integers
+  if ((R / 128 + E) * (N / 128) + E * (N / 64) >= INT32_MAX) return FP8B_EINVAL;
+  // token rows are gathered with 32-bit offsets from the start of a: the
+  // token matrix must stay below 4 GiB
+  if (T * K >= ((int64_t)1 << 32) || K >= kMaxLd) return FP8B_EINVAL;
   if (!aligned(a, 16) || !aligned(w, 16) || !aligned(y, 16)) return FP8B_EALIGN;
   if (!aligned(a_scales, 4) || !aligned(w_scales, 4) || !aligned(row_index, 4) || !aligned(expert_offsets, 4))
     return FP8B_EALIGN;

@@ -459,20 +459,23 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void block_gemm_kernel(
   const int lane = threadIdx.x & 63, wave = wave_id();
 
   Src<C> src;
-  // rows past M re-read the last row; their results are never stored
-  src.abase = A;
+  // 64-bit tile bases, 32-bit per-lane offsets inside the tile (the entry
+  // point keeps every leading dimension below 2^24); rows past M re-read
+  // the last row and their results are never stored
+  const int mlast = M - 1 - m0;
+  src.abase = A + (int64_t)m0 * lda;
   src.wbase = W + (int64_t)n0 * ldw;
-  make_code_src<C>(src, [&](int r) { return (uint32_t)(min(m0 + r, M - 1) * lda); },
+  make_code_src<C>(src, [&](int r) { return (uint32_t)(min(r, mlast) * lda); },
                    [&](int r) { return (uint32_t)(r * ldw); });
   src.scale_dst = -1;
-  src.sbase = reinterpret_cast<const uint8_t*>(SA);
+  src.sbase = reinterpret_cast<const uint8_t*>(SA + (int64_t)m0 * nkb);
   src.soff = 0;
   if (wave < C::NS_A) {
-    src.soff = (uint32_t)(min(m0 + 64 * wave + lane, M - 1) * nkb * 4);
+    src.soff = (uint32_t)(min(64 * wave + lane, mlast) * nkb * 4);
     src.scale_dst = C::OFF_SA + 256 * wave;
   } else if (wave == C::NS_A) {
-    src.sbase = reinterpret_cast<const uint8_t*>(SW);
-    src.soff = (uint32_t)((n0 / 128 + min(lane, C::BN / 128 - 1)) * nkb * 4);
+    src.sbase = reinterpret_cast<const uint8_t*>(SW + (int64_t)(n0 / 128) * nkb);
+    src.soff = (uint32_t)(min(lane, C::BN / 128 - 1) * nkb * 4);
     src.scale_dst = C::OFF_SB;
   }
 
@@ -496,20 +499,22 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void mx_gemm_kernel(
   const int srow = K / 32;  // E8M0 bytes per row
 
   Src<C> src;
-  src.abase = A;
+  // 64-bit tile bases, 32-bit per-lane offsets inside the tile
+  const int mlast = M - 1 - m0;
+  src.abase = A + (int64_t)m0 * lda;
   src.wbase = B + (int64_t)n0 * ldb;
-  make_code_src<C>(src, [&](int r) { return (uint32_t)(min(m0 + r, M - 1) * lda); },
+  make_code_src<C>(src, [&](int r) { return (uint32_t)(min(r, mlast) * lda); },
                    [&](int r) { return (uint32_t)(r * ldb); });
   src.scale_dst = -1;
-  src.sbase = EA;
+  src.sbase = EA + (int64_t)m0 * srow;
   src.soff = 0;
   if (wave < C::NS_A) {
-    src.soff = (uint32_t)(min(m0 + 64 * wave + lane, M - 1) * srow);
+    src.soff = (uint32_t)(min(64 * wave + lane, mlast) * srow);
     src.scale_dst = C::OFF_SA + 256 * wave;
   } else if (wave < C::NS) {
     const int t = wave - C::NS_A;
-    src.sbase = EB;
-    src.soff = (uint32_t)((n0 + 64 * t + lane) * srow);
+    src.sbase = EB + (int64_t)n0 * srow;
+    src.soff = (uint32_t)((64 * t + lane) * srow);
     src.scale_dst = C::OFF_SB + 256 * t;
   }
 
@@ -794,8 +799,8 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
         src.soff = (uint32_t)token(64 * wave + lane) * (uint32_t)(nkb * 4);
         src.scale_dst = C::OFF_SA + 256 * wave;
       } else if (wave == C::NS_A) {
-        src.sbase = reinterpret_cast<const uint8_t*>(SW + (int64_t)e * (N / 128) * nkb);
-        src.soff = (uint32_t)((n0 / 128 + min(lane, C::BN / 128 - 1)) * nkb * 4);
+        src.sbase = reinterpret_cast<const uint8_t*>(SW + ((int64_t)e * (N / 128) + n0 / 128) * nkb);
+        src.soff = (uint32_t)(min(lane, C::BN / 128 - 1) * nkb * 4);
         src.scale_dst = C::OFF_SB;
       }
       v4f acc[C::MI][C::NJ];

@@ -125,7 +125,8 @@ int fp8_weight_quant(const void *w, int64_t N, int64_t K, int64_t ld_w,
  *   a_scales  float [M][K/128], contiguous (fp8_act_quant with block 128).
  *   w         codes [N][ld_w], 16-byte aligned, ld_w % 16 == 0, >= K.
  *   w_scales  float [N/128][K/128], contiguous.
- *   M >= 0 (0 is a no-op); N, K > 0 and multiples of 128.
+ *   M >= 0 (0 is a no-op); N, K > 0 and multiples of 128;
+ *   ld_a, ld_w < 2^24.
  *   y         [M][ld_y] fp32 or bf16, 16-byte aligned, ld_y >= N,
  *             ld_y % 8 == 0.
  *   out_dtype FP8B_OUT_F32 or FP8B_OUT_BF16.
@@ -147,7 +148,7 @@ int fp8_block_gemm(const uint8_t *a, int64_t ld_a, const float *a_scales,
  *           ld % 16 == 0, ld >= K.
  *   a_e8m0  uint8 [M][K/32]; b_e8m0 uint8 [N][K/32]; contiguous, 4-byte
  *           aligned (fp8_act_quant with block 32, FP8B_SCALE_E8M0_BYTE).
- *   M >= 0; N, K > 0 and multiples of 128.
+ *   M >= 0; N, K > 0 and multiples of 128; ld_a, ld_b < 2^24.
  *   y       float [M][ld_y], 16-byte aligned, ld_y % 4 == 0, ld_y >= N.
  *   Scale byte 0xFF (NaN) gives unspecified outputs.
  */
@@ -176,7 +177,8 @@ int mxfp8_gemm(const uint8_t *a, int64_t ld_a, const uint8_t *a_e8m0,
  *   expert_offsets  int32 [E+1] (device), non-decreasing, [0] = 0,
  *                   [E] = R.  Entries outside that contract, or token ids
  *                   outside [0, T), give unspecified rows but never fault.
- *   T >= 1, R >= 0 (0 is a no-op), 1 <= E <= 1024.
+ *   T >= 1, R >= 0 (0 is a no-op), 1 <= E <= 1024; T * K < 2^32 (the
+ *   token matrix is gathered with 32-bit offsets).
  *   w               codes [E][N][K] (contiguous, 16-byte aligned).
  *   w_scales        float [E][N/128][K/128].
  *   N, K            > 0, multiples of 128.

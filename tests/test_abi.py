@@ -150,6 +150,8 @@ def test_block_gemm_validation(L):
     assert f(*bad) == -2                                                  # ld_a % 16
     bad = list(args); bad[6] = 0
     assert f(*bad) == 0                                                   # M = 0
+    bad = list(args); bad[1] = 1 << 24
+    assert f(*bad) == -1                                                  # ld_a >= 2^24
 
 
 def test_mx_and_grouped_and_cast_validation(L):
@@ -165,6 +167,8 @@ def test_mx_and_grouped_and_cast_validation(L):
     assert g(*bad) == -3
     bad = list(args); bad[5] = 0
     assert g(*bad) == 0                                                   # R = 0
+    bad = list(args); bad[2] = 1 << 20; bad[10] = 1 << 13
+    assert g(*bad) == -1                                                  # T * K >= 2^32
     assert L.fp8_cast_f32(GOOD, 10, 2, GOOD, NULL) == -3
     assert L.fp8_cast_f32(GOOD, 0, 0, GOOD, NULL) == 0
 

@@ -342,3 +342,38 @@ def test_grouped_max_experts(F, orc):
     case = _moe_counts_case(counts, T=96, N=128, K=256, seed=46)
     yg, yr, bnd = _moe_run(F, orc, case)
     assert_parity(yg, yr, bnd, True, "moe 1024 experts")
+
+
+def test_gemms_with_activations_beyond_4gib(F, orc):
+    """A 9000-row activation matrix with a 512 KiB row stride (4.7 GB):
+    rows past 8192 lie beyond 2^32 bytes from its start, so the tile bases
+    must be 64-bit.  Block-scaled and MX GEMMs, rows on both sides checked."""
+    M, K, N, ld = 9000, 256, 256, 1 << 19
+    g = W.gen(47)
+    x = W.activations(M, K, 2, 20.0, g)
+    w = W.weights(N, K, 0.02, g)
+    big = torch.zeros(M * ld, dtype=torch.uint8, device=DEV)
+    qa = big.view(M, ld)[:, :K]
+    sa = torch.empty(M, K // 128, dtype=torch.float32, device=DEV)
+    F.fp8_act_quant(x.to(DEV), 128, "fp32", q=qa, scales=sa)
+    wq, ws = F.fp8_weight_quant(w.to(DEV), "fp32")
+    y = F.fp8_block_gemm(qa, sa, wq, ws, torch.float32)
+    torch.cuda.synchronize()
+    rows = [0, 8191, 8192, 8960, M - 1]
+    oa, osa = orc.act_quant(W.bits(x[rows]), 128, 0)
+    ow, osw = orc.weight_quant(W.bits(w), 0)
+    yr, bnd = orc.block_gemm(oa, osa, ow, osw)
+    assert_parity(_np(y[rows]), yr, bnd, False, "block gemm, rows past 4 GiB")
+    # MX: the same strided storage for 32-blocks with E8M0 bytes
+    ea = torch.empty(M, K // 32, dtype=torch.uint8, device=DEV)
+    F.fp8_act_quant(x.to(DEV), 32, "e8m0", q=qa, scales=ea)
+    b = W.mx_operand(N, K, g)
+    qb, eb = F.fp8_act_quant(b.to(DEV), 32, "e8m0")
+    ym = F.mxfp8_gemm(qa, ea, qb, eb)
+    torch.cuda.synchronize()
+    oa, oea = orc.act_quant(W.bits(x[rows]), 32, 2)
+    ob, oeb = orc.act_quant(W.bits(b), 32, 2)
+    yr, bnd = orc.mx_gemm(oa, oea, ob, oeb)
+    assert_parity(_np(ym[rows]), yr, bnd, False, "mx gemm, rows past 4 GiB")
+    del big
+    torch.cuda.empty_cache()
