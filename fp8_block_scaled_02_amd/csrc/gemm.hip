@@ -254,9 +254,17 @@ __device__ __forceinline__ void compute_block(const uint8_t* buf, v4f (&acc)[C::
   for (int i = 0; i < C::MI; ++i) araw[i] = read_raw(buf, wm * C::TM + 16 * i + l16, g);
 #pragma unroll
   for (int j = 0; j < 2 && j < C::NJ; ++j) wraw[j] = read_raw(wt, wn * C::TN + 16 * j + l16, g);
+  // Only the first 32-wide K window of the activation fragments is widened
+  // up front; windows 1..3 are widened between the MFMAs of the first weight
+  // fragment, so the step does not open with a VALU-only burst that leaves
+  // the matrix unit idle.
+  auto widen_a = [&](int i, int k) {
+    const uint4& h = k < 2 ? araw[i].lo : araw[i].hi;
+    xf[i].k[k] = (k & 1) ? cvt8(h.z, h.w, 1.0f) : cvt8(h.x, h.y, 1.0f);
+  };
 #pragma unroll
   for (int i = 0; i < C::MI; ++i) {
-    xf[i] = widen(araw[i], 1.0f, 1.0f);
+    widen_a(i, 0);
     s[i] = sar[i] * sw0;
   }
   Frag16 wcur = widen(wraw[0], 1.0f, 1.0f), wnext;
@@ -272,6 +280,10 @@ __device__ __forceinline__ void compute_block(const uint8_t* buf, v4f (&acc)[C::
 #pragma unroll
       for (int i = 0; i < C::MI; ++i)
         p[i] = mfma_bf16(wcur.k[k], xf[i].k[k], k == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : p[i]);
+      if (j == 0 && k < 3) {
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i) widen_a(i, k + 1);
+      }
       if (j + 1 < C::NJ) {
         const uint4& h = k < 2 ? wraw[j + 1].lo : wraw[j + 1].hi;
         wnext.k[k] = (k & 1) ? cvt8(h.z, h.w, 1.0f) : cvt8(h.x, h.y, 1.0f);
@@ -287,6 +299,9 @@ __device__ __forceinline__ void compute_block(const uint8_t* buf, v4f (&acc)[C::
         if (j > 0) asm volatile("" : "+v"(wcur.k[k + 1]), "+v"(acc[k][j - 1]));
         if (j + 1 < C::NJ) asm volatile("" : "+v"(wcur.k[k + 1]), "+v"(wnext.k[k]));
         asm volatile("" : "+v"(wcur.k[k + 1]), "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]));
+        if (j == 0)
+          asm volatile("" : "+v"(wcur.k[k + 1]), "+v"(xf[0].k[k + 1]), "+v"(xf[1].k[k + 1]), "+v"(xf[2].k[k + 1]),
+                       "+v"(xf[3].k[k + 1]));
       }
     }
 #pragma unroll
