@@ -62,6 +62,7 @@ def lib():
         L.orc_dequant_one.restype = ctypes.c_uint16
         L.orc_dequant_one.argtypes = [ctypes.c_uint8, ctypes.c_float]
         L.orc_weight_dequant.argtypes = [_c_u8p, _i64, _i64, _i64, _c_f32p, _c_u16p, _i64]
+        L.orc_weight_pack.argtypes = [_c_u8p, _i64, _i64, _i64, _i64, _c_u8p]
         L.orc_kv_quant.argtypes = [_c_u16p, _i64, _i64, _i64, _c_u8p, _i64, _c_f32p]
         L.orc_kv_dequant.argtypes = [_c_u8p, _i64, _i64, _i64, _c_f32p, _c_u16p, _i64]
         L.orc_moe_combine.argtypes = [_c_u16p, _i64, _i64, _c_i32p, _c_f32p, _i64, _i64, _c_f64p, _c_f64p]
@@ -77,6 +78,7 @@ def lib():
             ctypes.POINTER(_c_u8p), ctypes.POINTER(_c_f32p), _i64, _i64,
             _c_i64p, _i64, _c_f64p, _c_f64p]
         L.orc_num_threads.restype = ctypes.c_int
+        L.orc_set_num_threads.argtypes = [ctypes.c_int]
         _LIB = L
     return _LIB
 
@@ -91,6 +93,11 @@ def _c(arr, dtype):
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's parallel loops use from now on (n >= 1)."""
+    lib().orc_set_num_threads(int(n))
 
 
 # ---- codecs --------------------------------------------------------------
@@ -170,6 +177,23 @@ def weight_dequant(q, scales):
     if rc != 0:
         raise ValueError("orc_weight_dequant rejected its arguments")
     return w
+
+
+def weight_pack(w):
+    """Codes uint8 [N, K] or [G, N, K] -> the packed byte order (same shape):
+    1 KB chunks (kc, p) of 16 rows x 64 codes at (kc*N/16 + p)*1024, byte
+    256g + 16r + b = code [16p + r][64kc + 16g + b] (a storage layout of the
+    GPU library; the oracle states it element by element)."""
+    w = _c(w, np.uint8)
+    shape = w.shape
+    if w.ndim == 2:
+        w = w[None]
+    G, N, K = w.shape
+    out = np.empty((G, N, K), np.uint8)
+    rc = lib().orc_weight_pack(_p(w, _c_u8p), G, N, K, K, _p(out, _c_u8p))
+    if rc != 0:
+        raise ValueError("orc_weight_pack rejected its arguments")
+    return out.reshape(shape)
 
 
 def dequant_one(code: int, d: float) -> int:

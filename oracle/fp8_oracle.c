@@ -24,6 +24,14 @@ int orc_num_threads(void) {
 #endif
 }
 
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* Codecs.  [P1] 1.1 and [P3] format tables: E4M3 = 1 sign, 4 exponent,     */
 /* 3 mantissa bits (bias 7, largest finite 448, NaN only); E5M2 = 1 sign,   */
@@ -274,6 +282,27 @@ uint16_t orc_dequant_one(uint8_t code, float d) {
   if (isnan(v)) return 0x7FC0u;
   p = (float)(v * (double)d);  /* exact product (<= 28 bits), one rounding */
   return round_f32_to_bf16(p);
+}
+
+/* The packed order, element by element: chunk (kc, p) holds the 16 x 64
+ * codes of rows 16p.., columns 64kc..; inside it, byte 256g + 16r + b. */
+int orc_weight_pack(const uint8_t *w, int64_t G, int64_t N, int64_t K,
+                    int64_t ldw, uint8_t *out) {
+  int64_t i;
+  if (!w || !out || G < 0 || N < 0 || K < 0) return -1;
+  if (N % 16 != 0 || K % 64 != 0 || ldw < K) return -1;
+  for (i = 0; i < G; ++i) {
+    int64_t kc, p, g, r, b;
+    for (kc = 0; kc < K / 64; ++kc)
+      for (p = 0; p < N / 16; ++p)
+        for (g = 0; g < 4; ++g)
+          for (r = 0; r < 16; ++r)
+            for (b = 0; b < 16; ++b) {
+              const int64_t row = i * N + 16 * p + r, col = 64 * kc + 16 * g + b;
+              out[i * N * K + (kc * (N / 16) + p) * 1024 + 256 * g + 16 * r + b] = w[row * ldw + col];
+            }
+  }
+  return 0;
 }
 
 int orc_weight_dequant(const uint8_t *q, int64_t N, int64_t K, int64_t ldq,

@@ -95,6 +95,15 @@ uint16_t orc_dequant_one(uint8_t code, float d);
 int orc_weight_dequant(const uint8_t *q, int64_t N, int64_t K, int64_t ldq,
                        const float *scales, uint16_t *w, int64_t ldw);
 
+/* ---- packed weight layout (a storage order of the GPU library, not part of
+ * the method: the GEMMs on packed weights compute the same y) --------------
+ * For each of G matrices [N][ldw] of codes: out[i*N*K + (kc*(N/16) + p)*1024
+ * + 256*g + 16*r + b] = w[i][16p + r][64kc + 16g + b] for kc < K/64,
+ * p < N/16, g < 4, r < 16, b < 16.  N a multiple of 16, K of 64, ldw >= K.
+ * Returns 0, or -1 on bad arguments. */
+int orc_weight_pack(const uint8_t *w, int64_t G, int64_t N, int64_t K,
+                    int64_t ldw, uint8_t *out);
+
 /* ---- KV cache ([P2] section 4: E5M2, one scale per token) ----------------
  * Per row t of x [T][D]: amax over the row, d = fp32(amax / 57344) (1 if
  * amax = 0), q = E5M2(clamp(fp32(x / d), +-57344)), scales[t] = d.
@@ -153,6 +162,8 @@ int orc_grouped_gemm(const uint8_t *a, const float *sa, int64_t T,
 
 /* number of OpenMP threads the oracle uses */
 int orc_num_threads(void);
+/* Threads the parallel loops use from now on (n >= 1; other values are ignored). */
+void orc_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
