@@ -3,9 +3,10 @@
 
 Headline ("step"): one prefill-shaped linear layer, 4096 tokens x 7168 ->
 18432, i.e. fp8_act_quant (per token, per 128 channels, fp32 scales) on the
-bf16 activations followed by fp8_block_gemm against E4M3 weights with
-128x128 fp32 block scales, bf16 output.  Weights are quantised once,
-outside the timed region (offline in the method).  Inputs are seeded
+bf16 activations followed by fp8_block_gemm_packed against E4M3 weights
+with 128x128 fp32 block scales, bf16 output.  Weights are quantised and
+put in the packed layout (fp8_weight_pack) once, outside the timed region
+(offline in the method; the layout changes no result).  Inputs are seeded
 synthetic tensors already resident in HBM.
 
 value = 2*M*N*K / (time per step), i.e. block-scaled FP8 GEMM TFLOP/s
@@ -14,14 +15,21 @@ including act_quant.
 The same JSON line carries
   roofline      for the dominant kernel (the block GEMM), its average
                 launch duration measured with events on its stream;
+                and, under measured_ceilings, what torch's bf16 GEMM
+                (hipBLASLt) reaches on the same shape and a 1 GiB device copy
+                reaches on this GPU;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same
-                workload (rank 0, one GPU only);
+                workload (rank 0, one GPU only), on all host threads and on
+                one;
   legs          the other rows of the hot path measured the same way:
-                decode-shaped GEMMs (M = 1, 8, 32, 128; K 8192 -> N 28672,
-                ue8m0 scales, weights rotated over two copies so the
-                256 MB last-level cache cannot serve them), the MXFP8 GEMM
-                (8192^3) and the grouped MoE GEMM (256 experts, 4096 tokens,
-                top-8, N 2048, K 7168), plus act_quant bandwidth.
+                the headline GEMM on row-major weights, decode-shaped GEMMs
+                (M = 1, 8, 32, 128; K 8192 -> N 28672, ue8m0 scales, weights
+                rotated over two copies so the 256 MB last-level cache
+                cannot serve them; packed and row-major), the MXFP8 GEMM
+                (8192^3), the grouped MoE GEMM (256 experts, 4096 tokens,
+                top-8, N 2048, K 7168) with the combine and the whole layer,
+                weight dequant, KV-cache quant/dequant and delayed scaling,
+                plus act_quant bandwidth.
 """
 import argparse
 import hashlib
@@ -45,8 +53,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-legs", action="store_true", help="time the headline step only")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the measured ceilings (torch bf16 GEMM on the same shape, 1 GiB device copy)")
     p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
-    p.add_argument("--only", default="", help="run one leg only: decode|mx|moe|dequant|kv|delayed")
+    p.add_argument("--only", default="", help="run one leg only: prefill|decode|mx|moe|dequant|kv|delayed")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (a kernel of known traffic, for "
                         "scaling profiler byte counters)")
@@ -142,7 +152,9 @@ def main():
     c = W.prefill_linear(device=dev)
     M, K = c.x.shape
     N = c.w.shape[0]
-    wq, ws = F.fp8_weight_quant(c.w, "fp32")
+    wq_rm, ws = F.fp8_weight_quant(c.w, "fp32")
+    wq = F.fp8_weight_pack(wq_rm)        # offline, like the quantisation: the packed layout
+    del wq_rm
     x = c.x
     a = torch.empty(M, K, dtype=torch.uint8, device=dev)
     sa = torch.empty(M, K // 128, dtype=torch.float32, device=dev)
@@ -150,7 +162,7 @@ def main():
 
     def step():
         F.fp8_act_quant(x, 128, "fp32", q=a, scales=sa)
-        F.fp8_block_gemm(a, sa, wq, ws, torch.bfloat16, y=y)
+        F.fp8_block_gemm_packed(a, sa, wq, ws, torch.bfloat16, y=y)
 
     for _ in range(args.warmup):
         step()
@@ -166,7 +178,8 @@ def main():
 
     # per-kernel device times on the same stream
     t_aq = timed_graph(torch, lambda: F.fp8_act_quant(x, 128, "fp32", q=a, scales=sa), max(args.steps, 10))
-    t_gemm = timed(torch, lambda: F.fp8_block_gemm(a, sa, wq, ws, torch.bfloat16, y=y), max(args.steps, 10))
+    t_gemm = timed(torch, lambda: F.fp8_block_gemm_packed(a, sa, wq, ws, torch.bfloat16, y=y),
+                   max(args.steps, 10))
     gemm_bytes = M * K + N * K + M * (K // 128) * 4 + (N // 128) * (K // 128) * 4 + M * N * 2
     aq_bytes = M * K * 2 + M * K + M * (K // 128) * 4
     achieved = flops / t_gemm / 1e12
@@ -179,7 +192,8 @@ def main():
     legs["prefill"] = {"act_quant_us": round(t_aq * 1e6, 2),
                        "act_quant_GBps": round(aq_bytes / t_aq / 1e9, 1),
                        "act_quant_hbm_frac": round(aq_bytes / t_aq / 1e9 / PEAK_HBM_GBS, 4),
-                       "gemm_us": round(t_gemm * 1e6, 2), "gemm_TFLOPs": round(achieved, 1)}
+                       "gemm_us": round(t_gemm * 1e6, 2), "gemm_TFLOPs": round(achieved, 1),
+                       "weights": "packed layout (fp8_weight_pack, offline)"}
     del c
 
     # ---- CPU baseline: the oracle on a bounded sample -----------------------------
@@ -204,7 +218,46 @@ def main():
                "cores": O.num_threads(), "kind": "oracle",
                "sample": f"act_quant + block GEMM of the first {rows} of {M} token rows "
                          f"(all {N} outputs, K {K}), {t_cpu:.1f} s"}
+        # the same oracle on one thread, over a sample sized to a few seconds
+        all_threads = O.num_threads()
+        rows1 = max(1, min(rows, int(rows * 4.0 / max(t_cpu * all_threads, 1e-3))))
+        O.set_num_threads(1)
+        try:
+            t0 = time.perf_counter()
+            oa, osa = O.act_quant(xb[:rows1], 128, 0)
+            O.block_gemm(oa, osa, ow, osw)
+            t_one = time.perf_counter() - t0
+        finally:
+            O.set_num_threads(all_threads)
+        cpu["single_thread"] = {"value": round(2.0 * rows1 * N * K / t_one / 1e12, 6), "unit": "TFLOP/s",
+                                "sample": f"first {rows1} token rows, {t_one:.1f} s"}
         del ow, osw, xb
+
+    # ---- measured ceilings on this GPU, beside the spec peaks ------------------------
+    # torch's bf16 GEMM (hipBLASLt) on the same shape: what a tuned library reaches
+    # on the MFMA instruction the products run on; and a 1 GiB device copy.
+    ceilings = None
+    if not args.no_ceilings:
+        wb = W.prefill_linear(device=dev).w                            # bf16 [N, K]
+        mm = lambda: torch.nn.functional.linear(x, wb)                  # noqa: E731
+        for _ in range(3):          # the first calls load and select the library's kernels
+            mm()
+        t_mm = timed(torch, mm, max(args.steps, 10))
+        del wb
+        torch.cuda.empty_cache()
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        t_cp = timed(torch, lambda: dst.copy_(src), 10)
+        del src, dst
+        torch.cuda.empty_cache()
+        copy_gbs = 2.0 * (1 << 30) / t_cp / 1e9
+        mm_tflops = flops / t_mm / 1e12
+        ceilings = {"bf16_gemm_torch_us": round(t_mm * 1e6, 2), "bf16_gemm_torch_TFLOPs": round(mm_tflops, 1),
+                    "block_gemm_vs_bf16_gemm_torch": round(achieved / mm_tflops, 4),
+                    "device_copy_GBps": round(copy_gbs, 1),
+                    "act_quant_vs_device_copy": round(aq_bytes / t_aq / 1e9 / copy_gbs, 4)}
+        roofline["measured_ceilings"] = ceilings
 
     del x, a, sa, y, wq, ws
     torch.cuda.empty_cache()
@@ -238,7 +291,8 @@ def main():
         "data": "synthetic",
         "pct_of_fp8_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
         "config": {"workload": "prefill linear: act_quant (per token per 128, fp32 scales) + "
-                               "block-scaled FP8 GEMM (128x128 fp32 weight scales), bf16 out",
+                               "block-scaled FP8 GEMM (128x128 fp32 weight scales, weights in the "
+                               "packed layout), bf16 out",
                    "M": M, "K": K, "N": N},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -250,30 +304,52 @@ def main():
 def run_legs(torch, F, W, dev, only=""):
     legs = {}
     iters = 20
+    if only in ("", "prefill"):
+        # the headline GEMM on row-major weight codes, for comparison
+        c = W.prefill_linear(device=dev)
+        M, K = c.x.shape
+        N = c.w.shape[0]
+        a, sa = F.fp8_act_quant(c.x, 128, "fp32")
+        wq, ws = F.fp8_weight_quant(c.w, "fp32")
+        del c
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        t = timed(torch, lambda: F.fp8_block_gemm(a, sa, wq, ws, torch.bfloat16, y=y), iters)
+        legs["prefill_row_major_weights"] = {"gemm_us": round(t * 1e6, 2),
+                                             "TFLOPs": round(2.0 * M * N * K / t / 1e12, 1)}
+        del a, sa, wq, ws, y
+        torch.cuda.empty_cache()
     if only in ("", "decode"):
         c = W.decode_linear(device=dev)
         K, N = c.x.shape[1], c.w.shape[0]
         copies = [F.fp8_weight_quant(c.w, "ue8m0") for _ in range(2)]   # > 256 MB together
+        packed = [(F.fp8_weight_pack(wq), ws) for wq, ws in copies]
         del c.w
         dec = {}
         for M in (1, 8, 32, 128):
             a, sa = F.fp8_act_quant(c.x[:M].contiguous(), 128, "ue8m0")
             y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-            st = [0]
-
-            def g():
-                wq, ws = copies[st[0] & 1]
-                st[0] += 1
-                F.fp8_block_gemm(a, sa, wq, ws, torch.bfloat16, y=y)
-            for _ in range(4):
-                g()
-            t = timed_graph(torch, g, iters)
             nbytes = N * K + (N // 128) * (K // 128) * 4 + M * K + M * (K // 128) * 4 + M * N * 2
+            res = {}
+            for layout, ws_list, gemm in (("packed", packed, F.fp8_block_gemm_packed),
+                                          ("row_major", copies, F.fp8_block_gemm)):
+                st = [0]
+
+                def g():
+                    wq, ws = ws_list[st[0] & 1]
+                    st[0] += 1
+                    gemm(a, sa, wq, ws, torch.bfloat16, y=y)
+                for _ in range(4):
+                    g()
+                res[layout] = timed_graph(torch, g, iters)
+            t = res["packed"]
             dec[f"M{M}"] = {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
                             "hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
-                            "TFLOPs": round(2.0 * M * N * K / t / 1e12, 2)}
+                            "TFLOPs": round(2.0 * M * N * K / t / 1e12, 2),
+                            "row_major_us": round(res["row_major"] * 1e6, 2),
+                            "row_major_GBps": round(nbytes / res["row_major"] / 1e9, 1)}
+        dec["weights"] = "packed layout (fp8_weight_pack); row_major_* = the same GEMM on row-major codes"
         legs["decode"] = dec
-        del copies, c
+        del copies, packed, c
         torch.cuda.empty_cache()
     if only in ("", "mx"):
         A, B = W.mx_case(device=dev)
@@ -304,7 +380,10 @@ def run_legs(torch, F, W, dev, only=""):
         ri, offs = case.row_index.to(dev), case.offs.to(dev)
         R = ri.shape[0]
         y = torch.empty(R, N, dtype=torch.bfloat16, device=dev)
-        t = timed(torch, lambda: F.fp8_grouped_gemm(a, sa, ri, offs, wq, ws, torch.bfloat16, y=y), iters)
+        t_rm = timed(torch, lambda: F.fp8_grouped_gemm(a, sa, ri, offs, wq, ws, torch.bfloat16, y=y), iters)
+        wq = F.fp8_weight_pack(wq)          # the layer runs on packed expert weights
+        torch.cuda.empty_cache()
+        t = timed(torch, lambda: F.fp8_grouped_gemm_packed(a, sa, ri, offs, wq, ws, torch.bfloat16, y=y), iters)
         counts = (case.offs[1:] - case.offs[:-1])
         active = int((counts > 0).sum())
         nbytes = active * (N * K + (N // 128) * (K // 128) * 4) + T * (K + K // 128 * 4) + R * N * 2
@@ -313,10 +392,11 @@ def run_legs(torch, F, W, dev, only=""):
         tr, gt = rt["token_rows"].to(dev), rt["gates"].to(dev)
         out = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
         t_c = timed_graph(torch, lambda: F.fp8_moe_combine(y, tr, gt, torch.bfloat16, out=out), iters)
-        t_l = timed(torch, lambda: F.moe_forward(case.x, ri, offs, tr, gt, wq, ws), iters)
+        t_l = timed(torch, lambda: F.moe_forward(case.x, ri, offs, tr, gt, wq, ws, packed=True), iters)
         cbytes = R * N * 2 + T * N * 2 + R * 8
         legs["moe"] = {"us": round(t * 1e6, 2), "TFLOPs": round(2.0 * R * N * K / t / 1e12, 1),
                        "GBps": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4),
+                       "row_major_us": round(t_rm * 1e6, 2), "weights": "packed layout (fp8_weight_pack)",
                        "active_experts": active, "max_rows": int(counts.max()),
                        "combine_us": round(t_c * 1e6, 2), "combine_GBps": round(cbytes / t_c / 1e9, 1),
                        "layer_us": round(t_l * 1e6, 2), "layer_TFLOPs": round(2.0 * R * N * K / t_l / 1e12, 1)}

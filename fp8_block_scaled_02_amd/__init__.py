@@ -62,6 +62,12 @@ def lib():
         L.mxfp8_gemm.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, i64, vp, i64, vp]
         L.fp8_grouped_gemm.restype = ci
         L.fp8_grouped_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp, i64, i64, vp, ci, vp]
+        L.fp8_weight_pack.restype = ci
+        L.fp8_weight_pack.argtypes = [vp, i64, i64, i64, i64, vp, vp]
+        L.fp8_block_gemm_packed.restype = ci
+        L.fp8_block_gemm_packed.argtypes = [vp, i64, vp, vp, vp, i64, i64, i64, vp, i64, ci, vp]
+        L.fp8_grouped_gemm_packed.restype = ci
+        L.fp8_grouped_gemm_packed.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp, i64, i64, vp, ci, vp]
         L.fp8_weight_dequant.restype = ci
         L.fp8_weight_dequant.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp]
         L.fp8_moe_combine.restype = ci
@@ -180,13 +186,15 @@ def fp8_moe_combine(y: torch.Tensor, token_rows: torch.Tensor, gates: torch.Tens
 
 
 def moe_forward(x: torch.Tensor, row_index, expert_offsets, token_rows, gates, w_q, w_scales,
-                out_dtype=torch.bfloat16):
+                out_dtype=torch.bfloat16, packed=False):
     """One block-scale MoE expert projection as a kernel sequence: act_quant
     of the tokens (once per token, per 128 channels, fp32 scales), the
     grouped GEMM over the routed rows (gather inside), then the gate-weighted
-    combine back to tokens.  Returns (out [T, N], y routed rows [R, N])."""
+    combine back to tokens.  packed: w_q is fp8_weight_pack of the expert
+    weights.  Returns (out [T, N], y routed rows [R, N])."""
     a, sa = fp8_act_quant(x, 128, "fp32")
-    y = fp8_grouped_gemm(a, sa, row_index, expert_offsets, w_q, w_scales, torch.bfloat16)
+    gemm = fp8_grouped_gemm_packed if packed else fp8_grouped_gemm
+    y = gemm(a, sa, row_index, expert_offsets, w_q, w_scales, torch.bfloat16)
     return fp8_moe_combine(y, token_rows, gates, out_dtype), y
 
 
@@ -264,6 +272,43 @@ def fp8_block_gemm(a, a_scales, w, w_scales, out_dtype=torch.bfloat16, y=None):
     return y
 
 
+def fp8_weight_pack(w: torch.Tensor, out=None):
+    """Weight codes uint8 [N, K] or [G, N, K] (row-major) -> the packed
+    layout read by fp8_block_gemm_packed / fp8_grouped_gemm_packed, returned
+    as a contiguous uint8 tensor of the same shape whose bytes are in packed
+    order (1 KB chunks of 16 rows x 64 codes, K outermost)."""
+    _need(w.dtype == torch.uint8 and w.dim() in (2, 3), "w must be uint8 [N, K] or [G, N, K]")
+    _need(w.stride(-1) == 1, "w rows must be contiguous")
+    G = 1 if w.dim() == 2 else w.shape[0]
+    N, K = w.shape[-2], w.shape[-1]
+    ld = w.stride(-2)
+    _need(w.dim() == 2 or G == 1 or w.stride(0) == N * ld, "matrices of w must be [N][ld] one after another")
+    if out is None:
+        out = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    _need(out.is_contiguous() and out.numel() == G * N * K, "out must be contiguous with G*N*K bytes")
+    rc = lib().fp8_weight_pack(_p(w), G, N, K, ld, _p(out), _stream(w))
+    _check("fp8_weight_pack", rc)
+    return out
+
+
+def fp8_block_gemm_packed(a, a_scales, w_packed, w_scales, out_dtype=torch.bfloat16, y=None):
+    """fp8_block_gemm with the weight codes from fp8_weight_pack (shape [N, K])."""
+    _need(a.dtype == torch.uint8 and w_packed.dtype == torch.uint8, "codes must be uint8")
+    _need(a_scales.dtype == torch.float32 and w_scales.dtype == torch.float32, "scales must be float32")
+    _need(w_packed.is_contiguous() and w_packed.dim() == 2, "w_packed must be a contiguous [N, K] tensor")
+    M, K = a.shape
+    N = w_packed.shape[0]
+    _need(w_packed.shape[1] == K, "w_packed must be [N, K]")
+    od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    if y is None:
+        y = torch.empty(M, N, dtype=out_dtype, device=a.device)
+    _need(y.stride(1) == 1, "y rows must be contiguous")
+    rc = lib().fp8_block_gemm_packed(_p(a), a.stride(0) if M else K, _p(a_scales), _p(w_packed), _p(w_scales),
+                                     M, N, K, _p(y), y.stride(0) if M else N, od, _stream(a))
+    _check("fp8_block_gemm_packed", rc)
+    return y
+
+
 def mxfp8_gemm(a, a_e8m0, b, b_e8m0, y=None):
     """y[M, N] (fp32) = MXFP8 GEMM of codes a [M, K], b [N, K] with E8M0
     bytes a_e8m0 [M, K/32], b_e8m0 [N, K/32]."""
@@ -296,6 +341,24 @@ def fp8_grouped_gemm(a, a_scales, row_index, expert_offsets, w, w_scales, out_dt
     return y
 
 
+def fp8_grouped_gemm_packed(a, a_scales, row_index, expert_offsets, w_packed, w_scales, out_dtype=torch.bfloat16,
+                            y=None):
+    """fp8_grouped_gemm with the expert weights from fp8_weight_pack (shape [E, N, K])."""
+    _need(row_index.dtype == torch.int32 and expert_offsets.dtype == torch.int32, "routing must be int32")
+    _need(a.is_contiguous() and w_packed.is_contiguous() and w_packed.dim() == 3,
+          "a and w_packed must be contiguous, w_packed [E, N, K]")
+    T, K = a.shape
+    E, N, _ = w_packed.shape
+    R = row_index.shape[0]
+    od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    if y is None:
+        y = torch.empty(R, N, dtype=out_dtype, device=a.device)
+    rc = lib().fp8_grouped_gemm_packed(_p(a), _p(a_scales), T, _p(row_index), _p(expert_offsets), R, E,
+                                       _p(w_packed), _p(w_scales), N, K, _p(y), od, _stream(a))
+    _check("fp8_grouped_gemm_packed", rc)
+    return y
+
+
 def fp8_cast_f32(x: torch.Tensor, fmt=FMT_E4M3, q=None):
     """FP8Cast with unit scale: clamp to +-Fmax, round to nearest even."""
     _need(x.dtype == torch.float32 and x.is_contiguous(), "x must be contiguous float32")
@@ -306,9 +369,11 @@ def fp8_cast_f32(x: torch.Tensor, fmt=FMT_E4M3, q=None):
     return q
 
 
-def linear(x: torch.Tensor, w_q, w_scales, scale_fmt="fp32", out_dtype=torch.bfloat16):
-    """W8A8 linear layer: act_quant(x) then the block-scaled GEMM."""
+def linear(x: torch.Tensor, w_q, w_scales, scale_fmt="fp32", out_dtype=torch.bfloat16, packed=False):
+    """W8A8 linear layer: act_quant(x) then the block-scaled GEMM (packed:
+    w_q is fp8_weight_pack of the weight codes)."""
     a, sa = fp8_act_quant(x, 128, scale_fmt)
     if sa.dtype != torch.float32:
         raise ValueError("the block GEMM takes fp32 or ue8m0 (fp32-stored) scales")
-    return fp8_block_gemm(a, sa, w_q, w_scales, out_dtype)
+    gemm = fp8_block_gemm_packed if packed else fp8_block_gemm
+    return gemm(a, sa, w_q, w_scales, out_dtype)

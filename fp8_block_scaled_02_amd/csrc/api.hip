@@ -12,6 +12,28 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every 32-bit tile index in range
 constexpr int64_t kMaxLd = (int64_t)1 << 24;   // GEMM leading dimensions: 32-bit offsets inside a tile
+constexpr int64_t kMaxPackedN = (int64_t)1 << 25;  // packed weights: 64 * N bytes per K chunk row, 32-bit
+
+// Arguments shared by the grouped GEMM entry points.
+int grouped_check(const uint8_t* a, const float* a_scales, int64_t T, const int32_t* row_index,
+                  const int32_t* expert_offsets, int64_t R, int64_t E, const uint8_t* w, const float* w_scales,
+                  int64_t N, int64_t K, void* y, int out_dtype) {
+  if (out_dtype != FP8B_OUT_F32 && out_dtype != FP8B_OUT_BF16) return FP8B_EUNSUPPORTED;
+  if (!a || !a_scales || !row_index || !expert_offsets || !w || !w_scales || !y) return FP8B_EINVAL;
+  if (T < 1 || R < 0 || E < 1 || E > 1024 || N <= 0 || K <= 0) return FP8B_EINVAL;
+  if (T > kMaxDim || R > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8B_EINVAL;
+  if (N % 128 != 0 || K % 128 != 0) return FP8B_EINVAL;
+  // the in-kernel work map counts tile items (128 x 128) and stream items
+  // (64 weight rows) in 32-bit integers
+  if ((R / 128 + E) * (N / 128) + E * (N / 64) >= INT32_MAX) return FP8B_EINVAL;
+  // token rows are gathered with 32-bit offsets from the start of a: the
+  // token matrix must stay below 4 GiB
+  if (T * K >= ((int64_t)1 << 32) || K >= kMaxLd) return FP8B_EINVAL;
+  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(y, 16)) return FP8B_EALIGN;
+  if (!aligned(a_scales, 4) || !aligned(w_scales, 4) || !aligned(row_index, 4) || !aligned(expert_offsets, 4))
+    return FP8B_EALIGN;
+  return FP8B_OK;
+}
 
 }  // namespace
 
@@ -71,7 +93,32 @@ FP8B_EXPORT int fp8_block_gemm(const uint8_t* a, int64_t ld_a, const float* a_sc
   if (((M + 127) / 128) * (N / 128) >= INT32_MAX) return FP8B_EINVAL;
   if (M == 0) return FP8B_OK;
   return fp8blk::launch_block_gemm(a, ld_a, a_scales, w, ld_w, w_scales, M, N, K, y, ld_y,
-                                   out_dtype == FP8B_OUT_BF16, as_stream(stream));
+                                   out_dtype == FP8B_OUT_BF16, false, as_stream(stream));
+}
+
+FP8B_EXPORT int fp8_weight_pack(const uint8_t* w, int64_t G, int64_t N, int64_t K, int64_t ld_w, uint8_t* w_packed,
+                                void* stream) {
+  if (!w || !w_packed) return FP8B_EINVAL;
+  if (G < 1 || N <= 0 || K <= 0 || G > kMaxDim || N > kMaxPackedN || K > kMaxDim) return FP8B_EINVAL;
+  if (N % 128 != 0 || K % 128 != 0 || ld_w < K) return FP8B_EINVAL;
+  if (!aligned(w, 16) || ld_w % 16 != 0 || !aligned(w_packed, 16)) return FP8B_EALIGN;
+  if (G * N / 256 * (K / 16) >= INT32_MAX) return FP8B_EINVAL;
+  return fp8blk::launch_weight_pack(w, G, N, K, ld_w, w_packed, as_stream(stream));
+}
+
+FP8B_EXPORT int fp8_block_gemm_packed(const uint8_t* a, int64_t ld_a, const float* a_scales, const uint8_t* w_packed,
+                                      const float* w_scales, int64_t M, int64_t N, int64_t K, void* y, int64_t ld_y,
+                                      int out_dtype, void* stream) {
+  if (out_dtype != FP8B_OUT_F32 && out_dtype != FP8B_OUT_BF16) return FP8B_EUNSUPPORTED;
+  if (!a || !a_scales || !w_packed || !w_scales || !y) return FP8B_EINVAL;
+  if (M < 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxPackedN || K > kMaxDim) return FP8B_EINVAL;
+  if (N % 128 != 0 || K % 128 != 0 || ld_a < K || ld_y < N || ld_a >= kMaxLd) return FP8B_EINVAL;
+  if (!aligned(a, 16) || !aligned(w_packed, 16) || ld_a % 16 != 0) return FP8B_EALIGN;
+  if (!aligned(a_scales, 4) || !aligned(w_scales, 4) || !aligned(y, 16) || ld_y % 8 != 0) return FP8B_EALIGN;
+  if (((M + 127) / 128) * (N / 128) >= INT32_MAX) return FP8B_EINVAL;
+  if (M == 0) return FP8B_OK;
+  return fp8blk::launch_block_gemm(a, ld_a, a_scales, w_packed, 0, w_scales, M, N, K, y, ld_y,
+                                   out_dtype == FP8B_OUT_BF16, true, as_stream(stream));
 }
 
 FP8B_EXPORT int mxfp8_gemm(const uint8_t* a, int64_t ld_a, const uint8_t* a_e8m0, const uint8_t* b, int64_t ld_b,
@@ -90,23 +137,23 @@ FP8B_EXPORT int mxfp8_gemm(const uint8_t* a, int64_t ld_a, const uint8_t* a_e8m0
 FP8B_EXPORT int fp8_grouped_gemm(const uint8_t* a, const float* a_scales, int64_t T, const int32_t* row_index,
                      const int32_t* expert_offsets, int64_t R, int64_t E, const uint8_t* w, const float* w_scales,
                      int64_t N, int64_t K, void* y, int out_dtype, void* stream) {
-  if (out_dtype != FP8B_OUT_F32 && out_dtype != FP8B_OUT_BF16) return FP8B_EUNSUPPORTED;
-  if (!a || !a_scales || !row_index || !expert_offsets || !w || !w_scales || !y) return FP8B_EINVAL;
-  if (T < 1 || R < 0 || E < 1 || E > 1024 || N <= 0 || K <= 0) return FP8B_EINVAL;
-  if (T > kMaxDim || R > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8B_EINVAL;
-  if (N % 128 != 0 || K % 128 != 0) return FP8B_EINVAL;
-  // the in-kernel work map counts tile items (128 x 128) and stream items
-  // (64 weight rows) in 32-bit integers
-  if ((R / 128 + E) * (N / 128) + E * (N / 64) >= INT32_MAX) return FP8B_EINVAL;
-  // token rows are gathered with 32-bit offsets from the start of a: the
-  // token matrix must stay below 4 GiB
-  if (T * K >= ((int64_t)1 << 32) || K >= kMaxLd) return FP8B_EINVAL;
-  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(y, 16)) return FP8B_EALIGN;
-  if (!aligned(a_scales, 4) || !aligned(w_scales, 4) || !aligned(row_index, 4) || !aligned(expert_offsets, 4))
-    return FP8B_EALIGN;
-  if (R == 0) return FP8B_OK;
+  const int rc = grouped_check(a, a_scales, T, row_index, expert_offsets, R, E, w, w_scales, N, K, y, out_dtype);
+  if (rc != FP8B_OK || R == 0) return rc;
   return fp8blk::launch_grouped_gemm(a, a_scales, T, row_index, expert_offsets, R, E, w, w_scales, N, K, y,
-                                     out_dtype == FP8B_OUT_BF16, as_stream(stream));
+                                     out_dtype == FP8B_OUT_BF16, false, as_stream(stream));
+}
+
+FP8B_EXPORT int fp8_grouped_gemm_packed(const uint8_t* a, const float* a_scales, int64_t T, const int32_t* row_index,
+                                        const int32_t* expert_offsets, int64_t R, int64_t E, const uint8_t* w_packed,
+                                        const float* w_scales, int64_t N, int64_t K, void* y, int out_dtype,
+                                        void* stream) {
+  const int rc =
+      grouped_check(a, a_scales, T, row_index, expert_offsets, R, E, w_packed, w_scales, N, K, y, out_dtype);
+  if (rc != FP8B_OK) return rc;
+  if (N > kMaxPackedN) return FP8B_EINVAL;
+  if (R == 0) return FP8B_OK;
+  return fp8blk::launch_grouped_gemm(a, a_scales, T, row_index, expert_offsets, R, E, w_packed, w_scales, N, K, y,
+                                     out_dtype == FP8B_OUT_BF16, true, as_stream(stream));
 }
 
 FP8B_EXPORT int fp8_weight_dequant(const uint8_t* q, int64_t N, int64_t K, int64_t ld_q, const float* scales, void* w,

@@ -27,15 +27,18 @@ int launch_delayed_quant(const void* x, int64_t n, void* state, int64_t L, int a
                          float* scale_used, hipStream_t s);
 int launch_weight_dequant(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, const float* scales,
                           void* w, int64_t ldw, hipStream_t s);
+int launch_weight_pack(const uint8_t* w, int64_t G, int64_t N, int64_t K, int64_t ldw, uint8_t* out,
+                       hipStream_t s);
+// packed: w is in the packed layout of launch_weight_pack (ldw unused)
 int launch_block_gemm(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w,
                       int64_t ldw, const float* sw, int64_t M, int64_t N, int64_t K, void* y,
-                      int64_t ldy, int out_bf16, hipStream_t s);
+                      int64_t ldy, int out_bf16, bool packed, hipStream_t s);
 int launch_mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* ea, const uint8_t* b,
                    int64_t ldb, const uint8_t* eb, int64_t M, int64_t N, int64_t K, float* y,
                    int64_t ldy, hipStream_t s);
 int launch_grouped_gemm(const uint8_t* a, const float* sa, int64_t T, const int32_t* row_index,
                         const int32_t* offs, int64_t R, int64_t E, const uint8_t* w,
                         const float* sw, int64_t N, int64_t K, void* y, int out_bf16,
-                        hipStream_t s);
+                        bool packed, hipStream_t s);
 
 }  // namespace fp8blk

@@ -14,8 +14,6 @@
 
 namespace fp8blk {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
 template <bool BF16>
 __global__ __launch_bounds__(256) void moe_combine_kernel(
     const uint16_t* __restrict__ y, int64_t R, int64_t N, const int32_t* __restrict__ token_rows,

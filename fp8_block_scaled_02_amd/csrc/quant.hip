@@ -18,9 +18,6 @@
 
 namespace fp8blk {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
 // FMT: 0 fp32 scales, 1 power-of-two scales stored as fp32, 2 E8M0 bytes.
 // Grid: x = token row, y = segment of 256 * UNROLL 16-byte chunks of the
 // row (so no index needs a division); each thread owns UNROLL chunks 256
@@ -208,6 +205,25 @@ __global__ __launch_bounds__(256) void weight_dequant_kernel(
   u32x4* dst = reinterpret_cast<u32x4*>(w + n * ldw + k);
   __builtin_nontemporal_store(u32x4{out[0], out[1], out[2], out[3]}, dst);
   __builtin_nontemporal_store(u32x4{out[4], out[5], out[6], out[7]}, dst + 1);
+}
+
+// Weight packing: G row-major code matrices [N][ld] -> the packed layout the
+// GEMMs can stream (chunk (kc, p) of 1 KB at (kc * N/16 + p) * 1024 holds
+// rows 16p .. 16p+15, K bytes 64kc .. 64kc+63, byte 256g + 16r + b = code
+// [16p + r][64kc + 16g + b]; matrix i at i * N * K).  A pure permutation,
+// done once per weight: each thread writes one 16-byte piece of the output
+// in order and reads its 16 codes from one row.
+__global__ __launch_bounds__(256) void weight_pack_kernel(
+    const uint8_t* __restrict__ w, int64_t G, int64_t N, int64_t K, int64_t ldw, uint8_t* __restrict__ out) {
+  const int64_t piece = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 16-byte output piece
+  const int64_t per_mat = N * K / 16;
+  if (piece >= G * per_mat) return;
+  const int64_t mat = piece / per_mat, in_mat = piece - mat * per_mat;
+  const int64_t chunk = in_mat >> 6, np = N / 16;
+  const int lane = (int)(in_mat & 63), r = lane & 15, g = lane >> 4;
+  const int64_t kc = chunk / np, p = chunk - kc * np;
+  const u32x4 v = *reinterpret_cast<const u32x4*>(w + (mat * N + 16 * p + r) * ldw + 64 * kc + 16 * g);
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + piece * 16));
 }
 
 // KV-cache quantisation ("LLM 推理的 FP8 混合精度工程 2026", section 4: the
@@ -449,6 +465,13 @@ int launch_weight_dequant(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, c
   const dim3 grid((unsigned)((N * (K / 16) + 255) / 256));
   hipLaunchKernelGGL(weight_dequant_kernel, grid, dim3(256), 0, s, q, N, K, ldq, scales,
                      static_cast<uint16_t*>(w), ldw);
+  return check_launch();
+}
+
+int launch_weight_pack(const uint8_t* w, int64_t G, int64_t N, int64_t K, int64_t ldw, uint8_t* out,
+                       hipStream_t s) {
+  const dim3 grid((unsigned)((G * N * (K / 16) + 255) / 256));
+  hipLaunchKernelGGL(weight_pack_kernel, grid, dim3(256), 0, s, w, G, N, K, ldw, out);
   return check_launch();
 }
 

@@ -137,6 +137,42 @@ int fp8_block_gemm(const uint8_t *a, int64_t ld_a, const float *a_scales,
                    int out_dtype, void *stream);
 
 /*
+ * fp8_weight_pack -- rearrange quantised weight codes into the packed
+ * layout that fp8_block_gemm_packed and fp8_grouped_gemm_packed read.  A
+ * storage layout of this library, not part of the method: the codes and
+ * their values are unchanged, only their order in memory.
+ *
+ * Layout of one [N][K] matrix (N*K bytes): 1024-byte chunks (kc, p) for
+ * kc < K/64, p < N/16, chunk (kc, p) at byte (kc * N/16 + p) * 1024; byte
+ * 256*g + 16*r + b of a chunk (g < 4, r < 16, b < 16) is the code of row
+ * 16p + r at column 64kc + 16g + b.  K is outermost, so a GEMM that
+ * streams the weights once reads them front to back, and each 64-lane
+ * 16-byte load is one contiguous chunk.  G matrices are packed one after
+ * the other (matrix i at i*N*K), e.g. the experts of a MoE layer.
+ *
+ *   w         codes [G][N][ld_w] (row-major, from fp8_weight_quant),
+ *             16-byte aligned, ld_w % 16 == 0, ld_w >= K.
+ *   G >= 1; N, K > 0 and multiples of 128; N <= 2^25.
+ *   w_packed  G*N*K bytes, 16-byte aligned, not overlapping w.
+ */
+int fp8_weight_pack(const uint8_t *w, int64_t G, int64_t N, int64_t K,
+                    int64_t ld_w, uint8_t *w_packed, void *stream);
+
+/*
+ * fp8_block_gemm_packed -- fp8_block_gemm (same operation, same passages,
+ * bit-identical output) with the weight codes in the packed layout of
+ * fp8_weight_pack.  Arguments as for fp8_block_gemm, except:
+ *
+ *   w_packed  N*K bytes from fp8_weight_pack (G = 1), 16-byte aligned.
+ *   N <= 2^25.
+ */
+int fp8_block_gemm_packed(const uint8_t *a, int64_t ld_a,
+                          const float *a_scales, const uint8_t *w_packed,
+                          const float *w_scales, int64_t M, int64_t N,
+                          int64_t K, void *y, int64_t ld_y, int out_dtype,
+                          void *stream);
+
+/*
  * mxfp8_gemm -- MXFP8 GEMM (ROCm 7.0 FP8 article, sections 1.1-1.2: blocks
  * of 32 elements along K share one E8M0 exponent).
  *
@@ -190,6 +226,19 @@ int fp8_grouped_gemm(const uint8_t *a, const float *a_scales, int64_t T,
                      int64_t R, int64_t E, const uint8_t *w,
                      const float *w_scales, int64_t N, int64_t K, void *y,
                      int out_dtype, void *stream);
+
+/*
+ * fp8_grouped_gemm_packed -- fp8_grouped_gemm (same operation, same
+ * passages, bit-identical output) with the expert weights in the packed
+ * layout: w_packed is fp8_weight_pack of the [E][N][K] codes with G = E
+ * (16-byte aligned).  Other arguments as for fp8_grouped_gemm; N <= 2^25.
+ */
+int fp8_grouped_gemm_packed(const uint8_t *a, const float *a_scales,
+                            int64_t T, const int32_t *row_index,
+                            const int32_t *expert_offsets, int64_t R,
+                            int64_t E, const uint8_t *w_packed,
+                            const float *w_scales, int64_t N, int64_t K,
+                            void *y, int out_dtype, void *stream);
 
 /*
  * fp8_moe_combine -- the gate-weighted combine after fp8_grouped_gemm,

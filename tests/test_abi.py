@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
     assert _declared() == sorted([
         "fp8b_abi_version", "fp8b_status_string", "fp8_act_quant", "fp8_weight_quant",
         "fp8_block_gemm", "mxfp8_gemm", "fp8_grouped_gemm", "fp8_moe_combine", "fp8_weight_dequant", "fp8_kv_quant", "fp8_kv_dequant",
-        "fp8_delayed_state_init", "fp8_delayed_quant", "fp8_cast_f32"])
+        "fp8_delayed_state_init", "fp8_delayed_quant", "fp8_cast_f32",
+        "fp8_weight_pack", "fp8_block_gemm_packed", "fp8_grouped_gemm_packed"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -171,6 +172,46 @@ def test_mx_and_grouped_and_cast_validation(L):
     assert g(*bad) == -1                                                  # T * K >= 2^32
     assert L.fp8_cast_f32(GOOD, 10, 2, GOOD, NULL) == -3
     assert L.fp8_cast_f32(GOOD, 0, 0, GOOD, NULL) == 0
+
+
+def test_packed_validation(L):
+    p = L.fp8_weight_pack
+    args = [GOOD, 2, 256, 384, 384, GOOD, NULL]
+    assert p(*args[:5], NULL, NULL) == -1                                 # no output
+    bad = list(args); bad[1] = 0
+    assert p(*bad) == -1                                                  # G = 0
+    bad = list(args); bad[2] = 200
+    assert p(*bad) == -1                                                  # N % 128
+    bad = list(args); bad[3] = 320
+    assert p(*bad) == -1                                                  # K % 128
+    bad = list(args); bad[4] = 256
+    assert p(*bad) == -1                                                  # ld_w < K
+    bad = list(args); bad[4] = 392
+    assert p(*bad) == -2                                                  # ld_w % 16
+    bad = list(args); bad[5] = ODD
+    assert p(*bad) == -2
+    bad = list(args); bad[2] = (1 << 25) + 128
+    assert p(*bad) == -1                                                  # N > 2^25
+    f = L.fp8_block_gemm_packed
+    args = [GOOD, 256, GOOD, GOOD, GOOD, 16, 256, 256, GOOD, 256, 1, NULL]
+    bad = list(args); bad[10] = 3
+    assert f(*bad) == -3
+    bad = list(args); bad[6] = 200
+    assert f(*bad) == -1                                                  # N % 128
+    bad = list(args); bad[3] = ODD
+    assert f(*bad) == -2                                                  # w_packed alignment
+    bad = list(args); bad[6] = (1 << 25) + 128
+    assert f(*bad) == -1                                                  # N > 2^25
+    bad = list(args); bad[5] = 0
+    assert f(*bad) == 0                                                   # M = 0
+    g = L.fp8_grouped_gemm_packed
+    args = [GOOD, GOOD, 16, GOOD, GOOD, 32, 4, GOOD, GOOD, 256, 256, GOOD, 1, NULL]
+    bad = list(args); bad[7] = ODD
+    assert g(*bad) == -2
+    bad = list(args); bad[9] = (1 << 25) + 128
+    assert g(*bad) == -1
+    bad = list(args); bad[5] = 0
+    assert g(*bad) == 0
 
 
 def test_binding_rejects_cpu_misuse():

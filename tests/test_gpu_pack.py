@@ -1,0 +1,170 @@
+"""GPU parity of the packed weight layout.
+
+fp8_weight_pack is a pure permutation: it must equal the oracle's
+element-by-element statement byte for byte.  The GEMMs on packed weights
+read the same fragments as on row-major weights, only from other
+addresses, so their outputs must be bit-identical to the row-major GEMMs
+(and meet the oracle tolerance, checked on a few cases directly)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def F():
+    import fp8_block_scaled_02_amd as F
+    assert torch.cuda.is_available()
+    return F
+
+
+def _same_bits(a, b, what):
+    assert a.shape == b.shape and a.dtype == b.dtype, what
+    ia = a.view(torch.int16 if a.dtype == torch.bfloat16 else torch.int32)
+    ib = b.view(torch.int16 if b.dtype == torch.bfloat16 else torch.int32)
+    bad = (ia != ib).nonzero()
+    assert bad.shape[0] == 0, f"{what}: {bad.shape[0]} outputs differ, first at {bad[0].tolist()}"
+
+
+@pytest.mark.parametrize("G,N,K,extra", [(1, 128, 128, 0), (1, 256, 384, 0), (3, 128, 256, 0), (1, 384, 640, 48)])
+def test_pack_matches_oracle(F, orc, G, N, K, extra):
+    rng = np.random.default_rng(G * N + K)
+    wide = rng.integers(0, 256, size=(G, N, K + extra), dtype=np.uint8)
+    w = torch.from_numpy(wide).to(DEV)[..., :K]          # row stride K + extra
+    if G == 1:
+        w = w[0]
+    got = F.fp8_weight_pack(w)
+    torch.cuda.synchronize()
+    want = orc.weight_pack(wide[..., :K] if G > 1 else wide[0, :, :K])
+    np.testing.assert_array_equal(got.cpu().numpy(), want)
+
+
+def _quant(F, c, fmt):
+    a, sa = F.fp8_act_quant(c.x.to(DEV), 128, fmt)
+    wq, ws = F.fp8_weight_quant(c.w.to(DEV), fmt)
+    return a, sa, wq, ws
+
+
+@pytest.mark.parametrize("M", [1, 3, 16, 17, 31, 32, 33, 64, 100, 128, 129, 300])
+@pytest.mark.parametrize("N,K", [(384, 640), (256, 1152)])
+def test_block_gemm_packed_is_bit_identical(F, M, N, K):
+    """Every kernel the block GEMM picks by M (streaming for M <= 16 and
+    <= 32, 64 x 128 tiles to 128, 128 x 128 tiles beyond) with ragged K
+    block counts, both output types."""
+    c = W.prefill_linear(M=M, N=N, K=K, seed=7 * M + N)
+    a, sa, wq, ws = _quant(F, c, "fp32")
+    wp = F.fp8_weight_pack(wq)
+    for out in (torch.bfloat16, torch.float32):
+        y0 = F.fp8_block_gemm(a, sa, wq, ws, out)
+        y1 = F.fp8_block_gemm_packed(a, sa, wp, ws, out)
+        torch.cuda.synchronize()
+        _same_bits(y1, y0, f"M {M} N {N} K {K} {out}")
+
+
+@pytest.mark.parametrize("M", [1, 20, 100, 260])
+def test_block_gemm_packed_meets_oracle(F, orc, M):
+    c = W.decode_linear(K=1152, N=512, seed=M)
+    x = c.x[:M] if M <= c.x.shape[0] else W.activations(M, 1152, 6, 50.0, W.gen(M))
+    a, sa = F.fp8_act_quant(x.to(DEV), 128, "ue8m0")
+    wq, ws = F.fp8_weight_quant(c.w.to(DEV), "ue8m0")
+    y = F.fp8_block_gemm_packed(a, sa, F.fp8_weight_pack(wq), ws, torch.bfloat16)
+    torch.cuda.synchronize()
+    oa, osa = orc.act_quant(W.bits(x), 128, 1)
+    ow, osw = orc.weight_quant(W.bits(c.w), 1)
+    yr, bnd = orc.block_gemm(oa, osa, ow, osw)
+    assert_parity(y.float().cpu().numpy().astype(np.float64), yr, bnd, True, f"packed M {M}")
+
+
+def test_block_gemm_packed_full_shapes(F):
+    """Decode (M 1, 8, 32, 128 at 8192 -> 28672, ue8m0) and prefill
+    (4096 x 7168 -> 18432, fp32 scales) at full size, as bench.py runs them."""
+    c = W.decode_linear(device=DEV)
+    a, sa, wq, ws = _quant(F, c, "ue8m0")
+    del c
+    wp = F.fp8_weight_pack(wq)
+    for M in (1, 8, 32, 128):
+        y0 = F.fp8_block_gemm(a[:M], sa[:M], wq, ws, torch.bfloat16)
+        y1 = F.fp8_block_gemm_packed(a[:M], sa[:M], wp, ws, torch.bfloat16)
+        torch.cuda.synchronize()
+        _same_bits(y1, y0, f"decode M {M}")
+    del a, sa, wq, ws, wp
+    c = W.prefill_linear(device=DEV)
+    a, sa, wq, ws = _quant(F, c, "fp32")
+    del c
+    wp = F.fp8_weight_pack(wq)
+    y0 = F.fp8_block_gemm(a, sa, wq, ws, torch.bfloat16)
+    y1 = F.fp8_block_gemm_packed(a, sa, wp, ws, torch.bfloat16)
+    torch.cuda.synchronize()
+    _same_bits(y1, y0, "prefill")
+
+
+def _moe_inputs(F, case):
+    x = case.x.to(DEV)
+    a, sa = F.fp8_act_quant(x, 128, "fp32")
+    E, N, K = case.w.shape
+    wq = torch.empty(E, N, K, dtype=torch.uint8, device=DEV)
+    ws = torch.empty(E, N // 128, K // 128, dtype=torch.float32, device=DEV)
+    for e in range(E):
+        F.fp8_weight_quant(case.w[e].to(DEV), "fp32", q=wq[e], scales=ws[e])
+    return a, sa, wq, ws, case.row_index.to(DEV), case.offs.to(DEV)
+
+
+def _counts_case(counts, T, N, K, seed):
+    counts = np.asarray(counts, np.int64)
+    g = W.gen(seed)
+    x = W.activations(T, K, max(1, round(0.005 * K)), 50.0, g)
+    w = torch.stack([W.weights(N, K, 0.02, g) for _ in counts])
+    offs = np.zeros(len(counts) + 1, np.int64)
+    offs[1:] = np.cumsum(counts)
+    ri = np.random.default_rng(seed).integers(0, T, size=int(offs[-1]))
+    experts = np.repeat(np.arange(len(counts)), counts)
+    return W.MoeCase(x, w, torch.from_numpy(ri.astype(np.int32)), torch.from_numpy(offs.astype(np.int32)),
+                     torch.from_numpy(experts.astype(np.int32)))
+
+
+@pytest.mark.parametrize("kind", ["tails", "short", "small"])
+def test_grouped_packed_is_bit_identical(F, orc, kind):
+    if kind == "tails":
+        case = _counts_case([0, 1, 16, 17, 32, 33, 127, 128, 129, 144, 160, 161, 256, 300, 0, 5], 200, 256, 640, 41)
+    elif kind == "short":
+        case = _counts_case([3, 0, 31, 7, 1, 0, 20, 16], 64, 384, 1152, 43)
+    else:
+        case = W.moe_case(T=64, E=8, topk=2, N=256, K=384)
+    a, sa, wq, ws, ri, offs = _moe_inputs(F, case)
+    wp = F.fp8_weight_pack(wq)
+    for out in (torch.bfloat16, torch.float32):
+        y0 = F.fp8_grouped_gemm(a, sa, ri, offs, wq, ws, out)
+        y1 = F.fp8_grouped_gemm_packed(a, sa, ri, offs, wp, ws, out)
+        torch.cuda.synchronize()
+        _same_bits(y1, y0, f"grouped {kind} {out}")
+    if kind == "tails":   # and against the oracle directly
+        E, N, K = case.w.shape
+        oa, osa = orc.act_quant(W.bits(case.x), 128, 0)
+        wl, sl = zip(*[orc.weight_quant(W.bits(case.w[e]), 0) for e in range(E)])
+        yr, bnd = orc.grouped_gemm(oa, osa, case.row_index.numpy(), case.offs.numpy(), list(wl), list(sl))
+        assert_parity(y1.float().cpu().numpy().astype(np.float64), yr, bnd, False, "grouped packed vs oracle")
+
+
+def test_grouped_packed_full_and_moe_forward(F):
+    """The full MoE shape (4096 tokens, 256 experts, top-8, 2048 x 7168) and
+    the whole layer (act_quant, grouped GEMM, combine) on packed weights."""
+    case = W.moe_case(device=DEV)
+    a, sa, wq, ws, ri, offs = _moe_inputs(F, case)
+    wp = F.fp8_weight_pack(wq)
+    y0 = F.fp8_grouped_gemm(a, sa, ri, offs, wq, ws, torch.bfloat16)
+    y1 = F.fp8_grouped_gemm_packed(a, sa, ri, offs, wp, ws, torch.bfloat16)
+    torch.cuda.synchronize()
+    _same_bits(y1, y0, "grouped full")
+    del y0, y1
+    T = case.x.shape[0]
+    r = W.routing_full(T, 256, 8, 1.0, W.gen(4))
+    tr, gates = r["token_rows"].to(DEV), r["gates"].to(DEV)
+    o0, _ = F.moe_forward(case.x, ri, offs, tr, gates, wq, ws)
+    o1, _ = F.moe_forward(case.x, ri, offs, tr, gates, wp, ws, packed=True)
+    torch.cuda.synchronize()
+    _same_bits(o1, o0, "moe_forward")
