@@ -24,6 +24,7 @@ FP8B_OK = 0
 SCALE_FP32, SCALE_UE8M0, SCALE_E8M0_BYTE = 0, 1, 2
 OUT_F32, OUT_BF16 = 0, 1
 FMT_E4M3, FMT_E5M2 = 0, 1
+DELAYED_HEADER_BYTES = 128 + 128 * 16    # FP8B_DELAYED_HEADER_BYTES of include/fp8blk.h
 
 _SCALE_FMT = {"fp32": SCALE_FP32, "ue8m0": SCALE_UE8M0, "e8m0": SCALE_E8M0_BYTE}
 
@@ -235,7 +236,7 @@ class DelayedScaler:
         self.history_len = int(history_len)
         self.algo = 0 if algo == "max" else 1
         self.divisor = float(divisor)
-        nbytes = 16 + 4 * self.history_len
+        nbytes = DELAYED_HEADER_BYTES + 4 * self.history_len
         self.state = torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
         self.reset()
 

@@ -315,72 +315,88 @@ __global__ __launch_bounds__(256) void kv_dequant_kernel(
 // memory, laid out as fp8b_delayed_state (scale, running amax bits, next
 // history slot, filled count, then the history), so a step is two kernels
 // in stream order and never needs the host.
+// Mirrors fp8b_delayed_state (include/fp8blk.h).
 struct DelayedHeader {
   float scale;
-  uint32_t step_amax;
+  uint32_t done;
   int32_t pos;
   int32_t filled;
+  uint32_t reserved[28];
+  uint32_t amax[FP8B_DELAYED_AMAX_SLOTS][32];
 };
+static_assert(sizeof(DelayedHeader) == FP8B_DELAYED_HEADER_BYTES, "state header layout");
+static_assert(sizeof(DelayedHeader) == sizeof(fp8b_delayed_state), "state header layout");
 
 __global__ __launch_bounds__(256) void delayed_init_kernel(uint8_t* __restrict__ st, int L) {
   DelayedHeader* h = reinterpret_cast<DelayedHeader*>(st);
   float* hist = reinterpret_cast<float*>(st + sizeof(DelayedHeader));
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < L) hist[i] = 0.0f;
+  if (i < FP8B_DELAYED_AMAX_SLOTS * 32) (&h->amax[0][0])[i] = 0u;
+  if (i < 28) h->reserved[i] = 0u;
   if (i == 0) {
     h->scale = 1.0f;
-    h->step_amax = 0u;
+    h->done = 0u;
     h->pos = 0;
     h->filled = 0;
   }
 }
 
-// Step part 1: codes = E4M3(clamp(x / d, +-448)) with the stored scale d
+// One step: codes = E4M3(clamp(x / d, +-448)) with the stored scale d
 // (IEEE division: d comes from another tensor, so the quotient can take any
-// magnitude), and the running amax of this step via one atomic max per
-// workgroup (non-negative floats order like their bit patterns).
+// magnitude), one chunk of 8192 values per workgroup.  Each workgroup folds
+// its amax into one of the state's 16 amax slots (workgroup b into slot
+// b mod 16) with an atomic max (non-negative floats order like their bit
+// patterns), then takes a ticket of its slot; the workgroup completing a
+// slot takes a ticket of the step, and the one completing the step has
+// every workgroup's maximum in the slots (each one's atomic max completed
+// before its tickets).  Spreading the atomics over 16 lines keeps them from
+// queueing on one word.  That workgroup closes the step: it merges and
+// clears the slots, pushes the amax into
+// the history, sets the next scale = h / divisor (1 if h = 0), h = the
+// window maximum (algo 0) or this step's amax (algo 1), and resets the
+// ticket.  Every workgroup has read the old scale before taking its ticket.
 constexpr int kDelayedUnroll = 4;
-constexpr int kDelayedMaxGroups = 1024;  // caps the atomics on the one amax word
 
-__global__ __launch_bounds__(256) void delayed_quant_kernel(
-    const uint16_t* __restrict__ x, int64_t n, const float* __restrict__ scale_in,
-    uint32_t* __restrict__ step_amax, uint8_t* __restrict__ q, float* __restrict__ scale_used) {
+__global__ __launch_bounds__(256) void delayed_step_kernel(
+    const uint16_t* __restrict__ x, int64_t n, uint8_t* __restrict__ st, int L, int algo, float divisor,
+    uint8_t* __restrict__ q, float* __restrict__ scale_used) {
+  DelayedHeader* hd = reinterpret_cast<DelayedHeader*>(st);
+  float* hist = reinterpret_cast<float*>(st + sizeof(DelayedHeader));
   __shared__ float red[4];
   const int tid = threadIdx.x;
-  const float d = *scale_in;
+  const float d = hd->scale;
   const int64_t nch = n / 8;
-  const int64_t stride = (int64_t)gridDim.x * 256 * kDelayedUnroll;
+  const int64_t base = (int64_t)blockIdx.x * 256 * kDelayedUnroll + tid;
   float amax = 0.0f;
-  for (int64_t base = (int64_t)blockIdx.x * 256 * kDelayedUnroll + tid; base < nch; base += stride) {
-    uint4 raw[kDelayedUnroll];
+  uint4 raw[kDelayedUnroll];
 #pragma unroll
-    for (int u = 0; u < kDelayedUnroll; ++u) {
-      const int64_t c = base + (int64_t)u * 256;
-      u32x4 v = {0, 0, 0, 0};
-      if (c < nch) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + 8 * c));
-      raw[u] = make_uint4(v[0], v[1], v[2], v[3]);
+  for (int u = 0; u < kDelayedUnroll; ++u) {
+    const int64_t c = base + (int64_t)u * 256;
+    u32x4 v = {0, 0, 0, 0};
+    if (c < nch) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + 8 * c));
+    raw[u] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+#pragma unroll
+  for (int u = 0; u < kDelayedUnroll; ++u) {
+    const int64_t c = base + (int64_t)u * 256;
+    const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
 #pragma unroll
-    for (int u = 0; u < kDelayedUnroll; ++u) {
-      const int64_t c = base + (int64_t)u * 256;
-      const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
-      float f[8];
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    if (c < nch) {
+      float v[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
-        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-      if (c < nch) {
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = clamp448(f[i] / d);
-        u32x2 out;
-        out[0] = pack4_e4m3(v[0], v[1], v[2], v[3]);
-        out[1] = pack4_e4m3(v[4], v[5], v[6], v[7]);
-        __builtin_nontemporal_store(out, reinterpret_cast<u32x2*>(q + 8 * c));
-      }
+      for (int i = 0; i < 8; ++i) v[i] = clamp448(f[i] / d);
+      u32x2 out;
+      out[0] = pack4_e4m3(v[0], v[1], v[2], v[3]);
+      out[1] = pack4_e4m3(v[4], v[5], v[6], v[7]);
+      __builtin_nontemporal_store(out, reinterpret_cast<u32x2*>(q + 8 * c));
     }
   }
   amax = row16_max(amax);
@@ -388,22 +404,44 @@ __global__ __launch_bounds__(256) void delayed_quant_kernel(
   amax = fmaxf(amax, __shfl_xor(amax, 32));
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
+  if (tid >= 64) return;  // one wave carries on
+  int closer = 0;
   if (tid == 0) {
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    atomicMax(step_amax, __float_as_uint(amax));
     if (blockIdx.x == 0) *scale_used = d;
+    // Slot sl's line holds its running maximum ([0]) and how many of its
+    // workgroups have finished ([1]).  Each atomic returns its old value,
+    // which proves it done; the empty asm statements (taking that value,
+    // clobbering memory) keep the next atomic behind it.  All are
+    // device-scope atomics, performed where every XCD sees them, so no
+    // fence is needed: the closing workgroup reads nothing else.
+    const int sl = (int)(blockIdx.x % FP8B_DELAYED_AMAX_SLOTS);
+    uint32_t* line = &hd->amax[sl][0];
+    const uint32_t prev = __hip_atomic_fetch_max(line, __float_as_uint(amax), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" ::"v"(prev) : "memory");
+    const uint32_t in_slot = (gridDim.x - sl + FP8B_DELAYED_AMAX_SLOTS - 1) / FP8B_DELAYED_AMAX_SLOTS;
+    const uint32_t t = __hip_atomic_fetch_add(line + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == in_slot - 1) {  // this slot is complete
+      asm volatile("" ::"v"(t) : "memory");
+      const uint32_t slots = min(gridDim.x, (unsigned)FP8B_DELAYED_AMAX_SLOTS);
+      closer = __hip_atomic_fetch_add(&hd->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == slots - 1;
+    }
   }
-}
+  if (!__shfl(closer, 0)) return;
 
-// Step part 2 (one wave): push this step's amax into the history and set
-// the next scale = h / divisor (1 if h = 0), h = the window maximum (algo
-// 0) or this step's amax (algo 1); reset the running amax.
-__global__ __launch_bounds__(64) void delayed_update_kernel(uint8_t* __restrict__ st, int L, int algo,
-                                                            float divisor) {
-  DelayedHeader* hd = reinterpret_cast<DelayedHeader*>(st);
-  float* hist = reinterpret_cast<float*>(st + sizeof(DelayedHeader));
-  const int lane = threadIdx.x;
-  const float a = __uint_as_float(hd->step_amax);
+  // the last workgroup, one wave: close the step
+  const int lane = tid;
+  uint32_t ab = 0u;
+  if (lane < FP8B_DELAYED_AMAX_SLOTS) {
+    ab = __hip_atomic_load(&hd->amax[lane][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&hd->amax[lane][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&hd->amax[lane][1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  float a = __uint_as_float(ab);
+  a = row16_max(a);
+  a = fmaxf(a, __shfl_xor(a, 16));
+  a = fmaxf(a, __shfl_xor(a, 32));
   const int pos = hd->pos;
   const int filled = min(hd->filled + 1, L);
   float h = a;
@@ -418,7 +456,7 @@ __global__ __launch_bounds__(64) void delayed_update_kernel(uint8_t* __restrict_
     hd->pos = (pos + 1) % L;
     hd->filled = filled;
     hd->scale = (h == 0.0f) ? 1.0f : h / divisor;
-    hd->step_amax = 0u;
+    __hip_atomic_store(&hd->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -500,21 +538,18 @@ int launch_kv_dequant(const uint8_t* q, int64_t T, int64_t D, int64_t ldq, const
 }
 
 int launch_delayed_init(void* state, int64_t L, hipStream_t s) {
-  hipLaunchKernelGGL(delayed_init_kernel, dim3((unsigned)((L + 255) / 256)), dim3(256), 0, s,
+  const int64_t words = std::max<int64_t>(L, FP8B_DELAYED_AMAX_SLOTS * 32);
+  hipLaunchKernelGGL(delayed_init_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s,
                      static_cast<uint8_t*>(state), (int)L);
   return check_launch();
 }
 
 int launch_delayed_quant(const void* x, int64_t n, void* state, int64_t L, int algo, float divisor, uint8_t* q,
                          float* scale_used, hipStream_t s) {
-  uint8_t* st = static_cast<uint8_t*>(state);
-  DelayedHeader* h = reinterpret_cast<DelayedHeader*>(st);
   const int64_t per_wg = 256 * kDelayedUnroll;
-  const dim3 grid((unsigned)std::min<int64_t>((n / 8 + per_wg - 1) / per_wg, kDelayedMaxGroups));
-  hipLaunchKernelGGL(delayed_quant_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(x), n, &h->scale,
-                     &h->step_amax, q, scale_used);
-  if (check_launch() != FP8B_OK) return FP8B_ELAUNCH;
-  hipLaunchKernelGGL(delayed_update_kernel, dim3(1), dim3(64), 0, s, st, (int)L, algo, divisor);
+  const dim3 grid((unsigned)((n / 8 + per_wg - 1) / per_wg));
+  hipLaunchKernelGGL(delayed_step_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(x), n,
+                     static_cast<uint8_t*>(state), (int)L, algo, divisor, q, scale_used);
   return check_launch();
 }
 

@@ -319,7 +319,8 @@ int fp8_kv_dequant(const uint8_t *q, int64_t T, int64_t D, int64_t ld_q,
  * history window (amax_history_len) and the "max" compute algorithm).
  * One scale per tensor.  The state is device memory owned by the caller:
  *
- *   fp8b_delayed_state header (16 bytes) followed by float history[len].
+ *   fp8b_delayed_state header (FP8B_DELAYED_HEADER_BYTES) followed by
+ *   float history[len].
  *
  * fp8_delayed_state_init writes the initial state (scale 1, empty history)
  * with a kernel (no memset, so it may be captured in a graph).
@@ -331,6 +332,10 @@ int fp8_kv_dequant(const uint8_t *q, int64_t T, int64_t D, int64_t ld_q,
  *   once `history_len` are held);
  *   state.scale = fp32(h / amax_divisor), or 1 if h = 0, where h is the
  *   history maximum (FP8B_AMAX_MAX) or this step's amax (FP8B_AMAX_LATEST).
+ *   One kernel does the whole step: the workgroup that finishes last
+ *   (counted through the amax slots and state.done) updates the history
+ *   and the scale, so the scale the next call reads is in place when this
+ *   call's work is done.
  *   Calls that share a state must be ordered (one stream); the same
  *   history_len must be passed to every call on a state.
  *
@@ -342,12 +347,21 @@ int fp8_kv_dequant(const uint8_t *q, int64_t T, int64_t D, int64_t ld_q,
  *   scale_used   float [1].
  */
 #define FP8B_DELAYED_MAX_HISTORY 65536
-#define FP8B_DELAYED_STATE_BYTES(len) (16 + 4 * (int64_t)(len))
+#define FP8B_DELAYED_AMAX_SLOTS 16
+#define FP8B_DELAYED_HEADER_BYTES (128 + 128 * FP8B_DELAYED_AMAX_SLOTS)
+#define FP8B_DELAYED_STATE_BYTES(len) (FP8B_DELAYED_HEADER_BYTES + 4 * (int64_t)(len))
 typedef struct {
   float scale;        /* the scale the next step uses                   */
-  uint32_t step_amax; /* running amax of a step in flight (float bits)  */
+  uint32_t done;      /* amax slots of a step in flight that completed  */
   int32_t pos;        /* next history slot                              */
   int32_t filled;     /* history entries written so far (<= len)       */
+  uint32_t reserved[28];
+  /* running amax of a step in flight, spread over slots so that the
+   * workgroups' atomics do not all meet on one word: slot s holds the
+   * float bits of its maximum in step_amax[s][0] and the number of its
+   * workgroups that finished in step_amax[s][1], one 128-byte line per
+   * slot; zero between steps */
+  uint32_t step_amax[FP8B_DELAYED_AMAX_SLOTS][32];
   /* float history[len] follows */
 } fp8b_delayed_state;
 typedef enum { FP8B_AMAX_MAX = 0, FP8B_AMAX_LATEST = 1 } fp8b_amax_algo;

@@ -337,6 +337,55 @@ def test_delayed_scaling_full_activation(F, orc):
         assert (_np(q) == q2[s]).all(), s
 
 
+@pytest.mark.parametrize("n", [8, 8 * 1000, 8192, 8192 * 3 + 40])
+def test_delayed_scaling_ragged_sizes(F, orc, n):
+    """One step is one kernel whose last workgroup closes the step: a single
+    partial workgroup, a ragged last workgroup, and exactly one full one."""
+    S = 6
+    x = _delayed_steps(S, n, n)
+    ds = F.DelayedScaler(4, "max", 400.0)
+    xd = x.to(DEV)
+    outs = [ds.quantize(xd[s]) for s in range(S)]
+    torch.cuda.synchronize()
+    q2, s2 = orc.delayed_scaling(W.bits(x), 4, 0, 400.0)
+    for s, (q, su) in enumerate(outs):
+        assert _np(su)[0] == s2[s], (n, s)
+        assert (_np(q) == q2[s]).all(), (n, s)
+
+
+def test_delayed_scaling_graph_replays(F, orc):
+    """A step captured in a HIP graph and replayed on new inputs, with eager
+    work and synchronisations between the replays, follows the oracle's
+    scale sequence at every replay."""
+    S, n = 6, 64 * 7168
+    x = _delayed_steps(S, n, 7).to(DEV)
+    ds = F.DelayedScaler(3, "max", 400.0)
+    buf = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    q = torch.empty(n, dtype=torch.uint8, device=DEV)
+    su = torch.empty(1, dtype=torch.float32, device=DEV)
+    buf.copy_(x[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):       # warm-up outside the graph, then restart the state
+        ds.quantize(buf, q=q, scale_used=su)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ds.reset()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ds.quantize(buf, q=q, scale_used=su)
+    ds.reset()                          # capture does not run the step
+    q2, s2 = orc.delayed_scaling(W.bits(x.cpu()), 3, 0, 400.0)
+    for s in range(S):
+        buf.copy_(x[s])
+        g.replay()
+        torch.cuda.synchronize()
+        assert _np(su)[0] == s2[s], s
+        assert (_np(q) == q2[s]).all(), s
+        _ = (x[s].float() * 2).sum().item()   # eager work between replays
+
+
 def test_act_quant_non_finite_blocks_stay_local(F, orc):
     """NaN and +-Inf inside some blocks: those blocks' codes and scales are
     unspecified, but every other block must still match the oracle exactly
