@@ -601,15 +601,18 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void mx_gemm_kernel(
 // from HBM and the math is small, so this path is built for bandwidth.  A
 // workgroup owns 64 weight rows (4 subtiles of 16 per wave) and up to 16*MI
 // activation rows; its 4 waves take every 4th K block, so together they read
-// contiguous 512-byte runs of each weight row.  Each wave loads its
-// fragments straight from global memory into a register ring kStreamDepth K
-// blocks ahead (no LDS staging, no barrier in the loop); the activation
-// fragments (L2 resident) are loaded once per K block and shared by the 4
-// weight subtiles.  The 4 partial sums are added in a fixed order through
-// LDS at the end.  Measured on MI355X (8192 -> 28672): 64 rows per
-// workgroup beat 16 and 32 by 10-45%, a deeper ring or a 2-way K split was
-// slower, and non-temporal weight loads were 10-15% slower (the two halves
-// of each 128-byte row segment come from different instructions).
+// contiguous 512-byte runs of each weight row (one contiguous front in the
+// packed layout).  Each wave loads its weight fragments straight from
+// global memory into a register ring kStreamDepth K blocks ahead (no
+// barrier in the loop).  The activation rows (L2 resident, read by every
+// workgroup) are loaded as whole 128-byte lines, eight lanes to a line, and
+// turned into MFMA fragments through a wave-private LDS tile: fragment-order
+// loads would split every line over two instructions and made M = 32 about
+// 20% slower than M = 16.  Each activation fragment is loaded once per K
+// block and shared by the 4 weight subtiles.  The 4 partial sums are added
+// in a fixed order through LDS at the end.  Measured on MI355X (8192 ->
+// 28672): 64 rows per workgroup beat 16 and 32 by 10-45%, and a deeper ring
+// or a 2-way K split was slower.
 constexpr int kStreamDepth = 2;
 constexpr int kStreamNJ = 4;
 constexpr int kStreamRows = 16 * kStreamNJ;  // weight rows per workgroup
@@ -644,45 +647,65 @@ __device__ __forceinline__ Raw16g load_frag_packed(const uint8_t* lane_base, int
   return v;
 }
 
+// Two whole 128-byte activation lines of a lane (rows r and r + 8 of a
+// fragment, bytes 16 * (lane & 7) ..), kept as native vectors.
+struct Lines2 {
+  u32x4 lo, hi;
+};
+
+__device__ __forceinline__ Lines2 load_lines(const uint8_t* p0, const uint8_t* p1) {
+  Lines2 v;
+  v.lo = *reinterpret_cast<const u32x4*>(p0);
+  v.hi = *reinterpret_cast<const u32x4*>(p1);
+  return v;
+}
+
 // LDS needed by stream_rows<MI>: partial sums of waves 1..3.
-template <int MI>
+template <int MI, int NJ = kStreamNJ>
 constexpr int stream_part_bytes() {
-  return 3 * MI * kStreamNJ * 64 * (int)sizeof(v4f);
+  return 3 * MI * NJ * 64 * (int)sizeof(v4f);
 }
 
 // acc[i][j] = y rows 16i + l16 of the chunk, weight rows 16j + 4g .. +3 of
-// the workgroup's 64, over all nkb K blocks.  arow[i] / sarow[i]: this
-// lane's activation row (codes, per-block scales); wload(j, kb): this lane's
-// fragment of weight subtile j at K block kb; swrow: the weight-scale row of
-// these 64 rows.  Every wave of the workgroup must call it; the sums are complete
+// the workgroup's 16*NJ, over all nkb K blocks.  aline[i][q]: row
+// 16i + 8q + (lane >> 3) of the activation codes at byte 16 * (lane & 7)
+// (eight lanes read each 128-byte line of a K block whole; the wave turns
+// the lines into its MFMA fragment through a private LDS tile in lds_a,
+// 4 * MI * 2048 bytes per workgroup); sarow[i]: the per-block scales of
+// this lane's row 16i + l16; wload(j, kb): this lane's fragment of weight
+// subtile j at K block kb; swrow: the weight-scale row of these rows.  Every wave of the workgroup must call it; the sums are complete
 // in wave 0 only (the return value says which), and `part` may be reused by
 // the caller only after a barrier.
-template <int MI, class WLoad>
-__device__ __forceinline__ bool stream_rows(const uint8_t* const (&arow)[MI], const float* const (&sarow)[MI],
-                                            WLoad wload, const float* swrow, int nkb,
-                                            v4f* part, v4f (&acc)[MI][kStreamNJ]) {
-  constexpr int D = kStreamDepth, NJ = kStreamNJ;
+template <int MI, int NJ = kStreamNJ, int D = kStreamDepth, class WLoad>
+__device__ __forceinline__ bool stream_rows(const uint8_t* const (&aline)[MI][2], const float* const (&sarow)[MI],
+                                            WLoad wload, const float* swrow, int nkb, uint8_t* lds_a,
+                                            v4f* part, v4f (&acc)[MI][NJ]) {
   const int lane = threadIdx.x & 63, ks = wave_id();
   const int nmine = ks < nkb ? (nkb - ks + 3) / 4 : 0;  // K blocks this wave adds
   // the t-th K block of this wave; t past the end repeats its last block
   auto kblock = [&](int t) { return ks + 4 * min(t, max(nmine - 1, 0)); };
 
-  Raw16g wr[D][NJ], ar[D][MI];
+  Raw16g wr[D][NJ];
+  Lines2 ar[D][MI];
   float sar[D][MI], swr[D];
   auto fetch = [&](int sl, int kb) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) wr[sl][j] = wload(j, kb);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      ar[sl][i] = load_frag_global(arow[i] + (int64_t)kb * kBK);
+      ar[sl][i] = load_lines(aline[i][0] + (int64_t)kb * kBK, aline[i][1] + (int64_t)kb * kBK);
       sar[sl][i] = sarow[i][kb];
     }
     swr[sl] = swrow[kb];
   };
-  if (nmine > 0) {
-#pragma unroll
-    for (int sl = 0; sl < D; ++sl) fetch(sl, kblock(sl));
-  }
+  // the ring slots are compile-time indices (the ring stays in registers)
+  auto each_slot = [&](auto f) {
+    f(std::integral_constant<int, 0>{});
+    if constexpr (D > 1) f(std::integral_constant<int, 1>{});
+    if constexpr (D > 2) f(std::integral_constant<int, 2>{});
+    static_assert(D <= 3, "ring depth");
+  };
+  if (nmine > 0) each_slot([&](auto slc) { fetch(decltype(slc)::value, kblock(decltype(slc)::value)); });
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -690,12 +713,18 @@ __device__ __forceinline__ bool stream_rows(const uint8_t* const (&arow)[MI], co
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int t0 = 0; t0 < nmine; t0 += D) {
-#pragma unroll
-    for (int sl = 0; sl < D; ++sl) {
+    each_slot([&](auto slc) {
+      constexpr int sl = decltype(slc)::value;
       if (t0 + sl < nmine) {
         Frag16 xf[MI];
 #pragma unroll
-        for (int i = 0; i < MI; ++i) xf[i] = widen(Raw16{ar[sl][i].lo, ar[sl][i].hi}, 1.0f, 1.0f);
+        for (int i = 0; i < MI; ++i) {
+          // lines -> fragment through the wave's swizzled 16 x 128-byte tile
+          uint8_t* la = lds_a + (ks * MI + i) * 2048;
+          *reinterpret_cast<u32x4*>(la + lds_off(lane >> 3, lane & 7)) = ar[sl][i].lo;
+          *reinterpret_cast<u32x4*>(la + lds_off(8 + (lane >> 3), lane & 7)) = ar[sl][i].hi;
+          xf[i] = widen(read_raw(la, lane & 15, lane >> 4), 1.0f, 1.0f);
+        }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           const Frag16 wf = widen(Raw16{wr[sl][j].lo, wr[sl][j].hi}, 1.0f, 1.0f);
@@ -709,7 +738,7 @@ __device__ __forceinline__ bool stream_rows(const uint8_t* const (&arow)[MI], co
         }
         fetch(sl, kblock(t0 + sl + D));  // refill this slot with the block D steps ahead
       }
-    }
+    });
   }
 
   if (ks > 0) {
@@ -735,8 +764,8 @@ __device__ __forceinline__ bool stream_rows(const uint8_t* const (&arow)[MI], co
 
 // Lane's outputs of stream_rows: chunk row 16i + l16 at element offset
 // row_off(16i + l16) of y (skipped when negative), columns n0 + 16j + 4g .. +3.
-template <int MI, bool BF16, class RowOff>
-__device__ __forceinline__ void stream_store(void* __restrict__ y, const v4f (&acc)[MI][kStreamNJ], int n0,
+template <int MI, bool BF16, int NJ = kStreamNJ, class RowOff>
+__device__ __forceinline__ void stream_store(void* __restrict__ y, const v4f (&acc)[MI][NJ], int n0,
                                              RowOff row_off) {
   const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -744,45 +773,48 @@ __device__ __forceinline__ void stream_store(void* __restrict__ y, const v4f (&a
     const int64_t base = row_off(16 * i + l16);
     if (base >= 0) {
 #pragma unroll
-      for (int j = 0; j < kStreamNJ; ++j) store4<BF16>(y, base + n0 + 16 * j + 4 * g, acc[i][j]);
+      for (int j = 0; j < NJ; ++j) store4<BF16>(y, base + n0 + 16 * j + 4 * g, acc[i][j]);
     }
   }
 }
 
-// Block GEMM for M <= 16*MI: one workgroup per 64 weight rows; W row-major
-// (PK false) or packed.
-template <int MI, bool BF16, bool PK>
+// Block GEMM for M <= 16*MI: one workgroup per 16*NJ weight rows, a
+// D-deep register ring; W row-major (PK false) or packed.
+template <int MI, bool BF16, bool PK, int NJ, int D>
 __global__ __launch_bounds__(256) void decode_gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ SA,
     const uint8_t* __restrict__ W, int64_t ldw, const float* __restrict__ SW, int M, int N, int K,
     void* __restrict__ Y, int64_t ldy) {
-  __shared__ v4f part[stream_part_bytes<MI>() / sizeof(v4f)];
-  const int l16 = threadIdx.x & 15;
-  const int n0 = blockIdx.x * kStreamRows, nkb = K / kBK;
-  const uint8_t* arow[MI];
+  __shared__ v4f part[stream_part_bytes<MI, NJ>() / sizeof(v4f)];
+  __shared__ __align__(16) uint8_t lds_a[4 * MI * 2048];
+  const int lane = threadIdx.x & 63, l16 = lane & 15;
+  const int n0 = blockIdx.x * 16 * NJ, nkb = K / kBK;
+  const uint8_t* aline[MI][2];
   const float* sarow[MI];
+  // rows past M repeat the last; never stored
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
-    const int m = min(16 * i + l16, M - 1);  // rows past M repeat the last; never stored
-    arow[i] = A + (int64_t)m * lda;
-    sarow[i] = SA + (int64_t)m * nkb;
+    sarow[i] = SA + (int64_t)min(16 * i + l16, M - 1) * nkb;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      aline[i][q] = A + (int64_t)min(16 * i + 8 * q + (lane >> 3), M - 1) * lda + 16 * (lane & 7);
   }
   const float* swrow = SW + (int64_t)(n0 / 128) * nkb;
-  v4f acc[MI][kStreamNJ];
+  v4f acc[MI][NJ];
   bool mine;
   if (PK) {
     const int64_t cs = (int64_t)(N / 16) * 1024;
     const uint8_t* wl = W + (int64_t)(n0 / 16) * 1024 + 16 * (threadIdx.x & 63);
-    mine = stream_rows<MI>(arow, sarow, [&](int j, int kb) { return load_frag_packed(wl, cs, j, kb); }, swrow,
-                           nkb, part, acc);
+    mine = stream_rows<MI, NJ, D>(aline, sarow, [&](int j, int kb) { return load_frag_packed(wl, cs, j, kb); },
+                                  swrow, nkb, lds_a, part, acc);
   } else {
     const uint8_t* wrow = W + (int64_t)(n0 + l16) * ldw;
-    mine = stream_rows<MI>(arow, sarow,
-                           [&](int j, int kb) { return load_frag_global(wrow + (int64_t)16 * j * ldw + (int64_t)kb * kBK); },
-                           swrow, nkb, part, acc);
+    mine = stream_rows<MI, NJ, D>(
+        aline, sarow, [&](int j, int kb) { return load_frag_global(wrow + (int64_t)16 * j * ldw + (int64_t)kb * kBK); },
+        swrow, nkb, lds_a, part, acc);
   }
   if (!mine) return;
-  stream_store<MI, BF16>(Y, acc, n0, [&](int r) -> int64_t { return r < M ? (int64_t)r * ldy : -1; });
+  stream_store<MI, BF16, NJ>(Y, acc, n0, [&](int r) -> int64_t { return r < M ? (int64_t)r * ldy : -1; });
 }
 
 // ---- grouped (MoE) GEMM -----------------------------------------------------
@@ -813,6 +845,7 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
     const uint8_t* __restrict__ W, const float* __restrict__ SW, int N, int K, void* __restrict__ Y) {
   static_assert(C::NT == 256, "stream items use 4 waves");
   static_assert(stream_part_bytes<2>() <= C::BUF, "stream partials fit in one stage");
+  static_assert(4 * 2 * 2048 <= C::BUF, "stream activation tiles fit in one stage");
   FP8B_STAGES(C);
   __shared__ int tstart[kMaxExperts + 1];  // first tile item of expert e
   __shared__ int sstart[kMaxExperts + 1];  // first stream item of expert e
@@ -930,23 +963,25 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
       auto row_off = [&](int r) -> int64_t { return r < t ? (int64_t)(r0 + r) * N : -1; };
       auto run = [&](auto mi) {
         constexpr int MI = decltype(mi)::value;
-        const uint8_t* arow[MI];
+        auto token = [&](int r) { return min(max(RI[r0 + min(r, t - 1)], 0), T - 1); };
+        const uint8_t* aline[MI][2];
         const float* sarow[MI];
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-          const int tok = min(max(RI[r0 + min(16 * i + l16, t - 1)], 0), T - 1);
-          arow[i] = A + (int64_t)tok * K;
-          sarow[i] = SA + (int64_t)tok * nkb;
+          sarow[i] = SA + (int64_t)token(16 * i + l16) * nkb;
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            aline[i][q] = A + (int64_t)token(16 * i + 8 * q + (lane >> 3)) * K + 16 * (lane & 7);
         }
         v4f acc[MI][kStreamNJ];
         bool mine;
         if (PK)
-          mine = stream_rows<MI>(arow, sarow, [&](int j, int kb) { return load_frag_packed(wrow, cs, j, kb); },
-                                 swrow, nkb, part, acc);
+          mine = stream_rows<MI>(aline, sarow, [&](int j, int kb) { return load_frag_packed(wrow, cs, j, kb); },
+                                 swrow, nkb, lds1, part, acc);
         else
-          mine = stream_rows<MI>(arow, sarow, [&](int j, int kb) {
+          mine = stream_rows<MI>(aline, sarow, [&](int j, int kb) {
             return load_frag_global(wrow + (int64_t)16 * j * K + (int64_t)kb * kBK);
-          }, swrow, nkb, part, acc);
+          }, swrow, nkb, lds1, part, acc);
         if (mine) stream_store<MI, BF16>(Y, acc, n0, row_off);
       };
       if (t <= 16)
@@ -993,17 +1028,33 @@ static int cu_count() {
   return n;
 }
 
+#ifndef FP8B_DEC1
+#define FP8B_DEC1 4, 2
+#endif
+#ifndef FP8B_DEC2
+#define FP8B_DEC2 4, 2
+#endif
+template <int MI, bool PK, int NJ, int D>
+static void launch_decode_nj(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
+                             const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
+                             hipStream_t s) {
+  const dim3 grid((unsigned)(N / (16 * NJ))), block(256);
+  if (out_bf16)
+    hipLaunchKernelGGL((decode_gemm_kernel<MI, true, PK, NJ, D>), grid, block, 0, s, a, lda, sa, w, ldw, sw,
+                       (int)M, (int)N, (int)K, y, ldy);
+  else
+    hipLaunchKernelGGL((decode_gemm_kernel<MI, false, PK, NJ, D>), grid, block, 0, s, a, lda, sa, w, ldw, sw,
+                       (int)M, (int)N, (int)K, y, ldy);
+}
+
 template <int MI, bool PK>
 static void launch_decode(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
                           const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
                           hipStream_t s) {
-  const dim3 grid((unsigned)(N / kStreamRows)), block(256);
-  if (out_bf16)
-    hipLaunchKernelGGL((decode_gemm_kernel<MI, true, PK>), grid, block, 0, s, a, lda, sa, w, ldw, sw, (int)M,
-                       (int)N, (int)K, y, ldy);
+  if (MI == 1)
+    launch_decode_nj<1, PK, FP8B_DEC1>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
   else
-    hipLaunchKernelGGL((decode_gemm_kernel<MI, false, PK>), grid, block, 0, s, a, lda, sa, w, ldw, sw, (int)M,
-                       (int)N, (int)K, y, ldy);
+    launch_decode_nj<2, PK, FP8B_DEC2>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
 }
 
 template <class C, bool PK>
