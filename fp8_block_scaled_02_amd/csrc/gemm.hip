@@ -1015,7 +1015,10 @@ using BlockCfg = Cfg<FP8B_BLOCK_CFG, false, FP8B_BLOCK_STAGES>;
 // 33 <= M <= 128: 64 x 128 tiles (4 waves of 64 x 32), twice the tiles of
 // 128 x 128 so a decode-sized layer fills the chip (measured at 8192 ->
 // 28672: M 64 93 -> 72 us, M 128 95 -> 89 us; three stages were slower).
-using SmallMCfg = Cfg<64, 128, 1, 4, false, 2>;
+#ifndef FP8B_SMALL_CFG
+#define FP8B_SMALL_CFG 64, 128, 1, 4, false, 2
+#endif
+using SmallMCfg = Cfg<FP8B_SMALL_CFG>;
 using MxCfg = Cfg<FP8B_MX_CFG, true, FP8B_MX_STAGES>;
 using MxSmallCfg = Cfg<128, 128, 2, 2, true, 2>;
 using GroupedCfg = Cfg<128, 128, 2, 2, false, 2>;
