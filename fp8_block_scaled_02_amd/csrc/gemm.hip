@@ -366,7 +366,9 @@ __device__ __forceinline__ void compute_block(const uint8_t* buf, v4f (&acc)[C::
 // 2^(e - 127) for an E8M0 byte e in [1, 254] (fp32 normal); e = 0 gives
 // 2^-127 (fp32 subnormal).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
-  return e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
+  // 2^-127 (the fp32 subnormal 0x00400000) times 2^e: exact for every
+  // byte 0..254, one v_ldexp_f32
+  return __builtin_amdgcn_ldexpf(__uint_as_float(0x00400000u), (int)e);
 }
 
 // One K step of the MXFP8 GEMM.  Each 32-block's E8M0 scale is folded into
