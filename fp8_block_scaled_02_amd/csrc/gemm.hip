@@ -1014,9 +1014,10 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
 #define FP8B_MX_STAGES 2
 #endif
 using BlockCfg = Cfg<FP8B_BLOCK_CFG, false, FP8B_BLOCK_STAGES>;
-// 33 <= M <= 128: 64 x 128 tiles (4 waves of 64 x 32), twice the tiles of
-// 128 x 128 so a decode-sized layer fills the chip (measured at 8192 ->
-// 28672: M 64 93 -> 72 us, M 128 95 -> 89 us; three stages were slower).
+// M up to 128 past the streaming kernel: 64 x 128 tiles (4 waves of
+// 64 x 32), twice the tiles of 128 x 128 so a decode-sized layer fills the
+// chip (measured at 8192 -> 28672: M 64 93 -> 72 us, M 128 95 -> 89 us;
+// three stages were slower).
 #ifndef FP8B_SMALL_CFG
 #define FP8B_SMALL_CFG 64, 128, 1, 4, false, 2
 #endif
@@ -1037,7 +1038,23 @@ static int cu_count() {
 #define FP8B_DEC1 4, 2
 #endif
 #ifndef FP8B_DEC2
-#define FP8B_DEC2 4, 2
+#define FP8B_DEC2 4, 1
+#endif
+// Streaming-kernel shapes per 16-token subtile count MI: (weight subtiles
+// per wave NJ, register ring depth D).  Measured on MI355X at 8192 ->
+// 28672 on packed weights: one subtile keeps a 2-deep ring (M 1: 39.9 us
+// against 41.4 with 1); from two subtiles on a 1-deep ring wins, its
+// registers leaving room for more waves (M 32: 47.4 -> 42.9 us), and the
+// streaming kernel beats the 64 x 128 tiles up to M = 64 (M 33 / 48 / 49:
+// 47.3 / 51.4 / 57.6 us against 62.3 / 62.5 / 62.8).
+#ifndef FP8B_STREAM_MAX_M
+#define FP8B_STREAM_MAX_M 64
+#endif
+#ifndef FP8B_DEC3
+#define FP8B_DEC3 4, 1
+#endif
+#ifndef FP8B_DEC4
+#define FP8B_DEC4 4, 1
 #endif
 template <int MI, bool PK, int NJ, int D>
 static void launch_decode_nj(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
@@ -1058,8 +1075,12 @@ static void launch_decode(const uint8_t* a, int64_t lda, const float* sa, const 
                           hipStream_t s) {
   if (MI == 1)
     launch_decode_nj<1, PK, FP8B_DEC1>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
-  else
+  else if (MI == 2)
     launch_decode_nj<2, PK, FP8B_DEC2>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+  else if (MI == 3)
+    launch_decode_nj<3, PK, FP8B_DEC3>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+  else
+    launch_decode_nj<4, PK, FP8B_DEC4>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
 }
 
 template <class C, bool PK>
@@ -1080,11 +1101,15 @@ template <bool PK>
 static void launch_block_any(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
                              const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
                              hipStream_t s) {
-  // M <= 32: the streaming kernel (one or two 16-token subtiles)
+  // M <= 64: the streaming kernel (one to four 16-token subtiles)
   if (M <= 16)
     launch_decode<1, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
   else if (M <= 32)
     launch_decode<2, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+  else if (FP8B_STREAM_MAX_M >= 48 && M <= 48)
+    launch_decode<3, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+  else if (FP8B_STREAM_MAX_M >= 64 && M <= 64)
+    launch_decode<4, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
   else if (M <= 128)
     launch_block<SmallMCfg, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
   else

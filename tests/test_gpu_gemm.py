@@ -63,11 +63,13 @@ def test_block_gemm_ragged(F, orc, M, N, K, out):
 
 @pytest.mark.parametrize("M,N,K", [(1, 512, 1152), (2, 256, 640), (1, 128, 128), (2, 384, 2176),
                                    (7, 384, 640), (16, 128, 128), (17, 256, 384),
-                                   (20, 256, 1152), (32, 640, 2048)])
+                                   (20, 256, 1152), (32, 640, 2048), (33, 256, 640), (40, 128, 128),
+                                   (48, 384, 1152), (49, 256, 384), (64, 640, 2048), (65, 256, 640)])
 def test_block_gemm_few_tokens(F, orc, M, N, K):
-    """M <= 32 takes the streaming decode kernel: one and two 16-token
-    subtiles, K-block counts below, at and past the prefetch depth and not a
-    multiple of the K split."""
+    """M <= 64 takes the streaming decode kernel: one to four 16-token
+    subtiles (2- and 1-deep register rings), K-block counts below, at and
+    past the prefetch depth and not a multiple of the K split; M = 65 is the
+    first size on 64 x 128 tiles."""
     c = W.decode_linear(K=K, N=N, seed=M + K)
     yg, yr, bnd = _linear_case(F, orc, c.x[:M], c.w, "ue8m0", torch.bfloat16)
     assert_parity(yg, yr, bnd, True, f"{M}x{N}x{K}")
@@ -86,7 +88,7 @@ def test_block_gemm_decode_full(F, orc):
     a, sa = F.fp8_act_quant(c.x, 128, "ue8m0")
     wq, ws = F.fp8_weight_quant(c.w, "ue8m0")
     ow, osw = orc.weight_quant(W.bits(c.w), 1)
-    for M in (1, 8, 32, 128):
+    for M in (1, 8, 32, 48, 64, 128):
         y = F.fp8_block_gemm(a[:M], sa[:M], wq, ws, torch.bfloat16)
         torch.cuda.synchronize()
         rows = sorted({0, M - 1, M // 2})

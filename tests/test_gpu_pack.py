@@ -50,7 +50,7 @@ def _quant(F, c, fmt):
     return a, sa, wq, ws
 
 
-@pytest.mark.parametrize("M", [1, 3, 16, 17, 31, 32, 33, 64, 100, 128, 129, 300])
+@pytest.mark.parametrize("M", [1, 3, 16, 17, 31, 32, 33, 47, 48, 49, 64, 65, 100, 128, 129, 300])
 @pytest.mark.parametrize("N,K", [(384, 640), (256, 1152)])
 def test_block_gemm_packed_is_bit_identical(F, M, N, K):
     """Every kernel the block GEMM picks by M (streaming for M <= 16 and
@@ -64,6 +64,25 @@ def test_block_gemm_packed_is_bit_identical(F, M, N, K):
         y1 = F.fp8_block_gemm_packed(a, sa, wp, ws, out)
         torch.cuda.synchronize()
         _same_bits(y1, y0, f"M {M} N {N} K {K} {out}")
+
+
+@pytest.mark.parametrize("M", [5, 30, 90, 200])
+def test_block_gemm_packed_strided_activations(F, M):
+    """Activation rows with a leading dimension above K (a column slice of a
+    wider code matrix), on each kernel the block GEMM picks by M."""
+    K, N, extra = 640, 384, 128
+    c = W.prefill_linear(M=M, N=N, K=K, seed=11 * M)
+    a, sa, wq, ws = _quant(F, c, "fp32")
+    wide = torch.zeros(M, K + extra, dtype=torch.uint8, device=DEV)
+    wide[:, :K] = a
+    wide[:, K:] = 0x7E                    # garbage past K must never be read
+    a_view = wide[:, :K]
+    assert a_view.stride(0) == K + extra
+    wp = F.fp8_weight_pack(wq)
+    y0 = F.fp8_block_gemm(a, sa, wq, ws, torch.bfloat16)
+    y1 = F.fp8_block_gemm_packed(a_view, sa, wp, ws, torch.bfloat16)
+    torch.cuda.synchronize()
+    _same_bits(y1, y0, f"strided M {M}")
 
 
 @pytest.mark.parametrize("M", [1, 20, 100, 260])
@@ -87,7 +106,7 @@ def test_block_gemm_packed_full_shapes(F):
     a, sa, wq, ws = _quant(F, c, "ue8m0")
     del c
     wp = F.fp8_weight_pack(wq)
-    for M in (1, 8, 32, 128):
+    for M in (1, 8, 32, 48, 64, 128):
         y0 = F.fp8_block_gemm(a[:M], sa[:M], wq, ws, torch.bfloat16)
         y1 = F.fp8_block_gemm_packed(a[:M], sa[:M], wp, ws, torch.bfloat16)
         torch.cuda.synchronize()
