@@ -1040,15 +1040,17 @@ static int cu_count() {
 #ifndef FP8B_DEC2
 #define FP8B_DEC2 4, 1
 #endif
-// Streaming-kernel shapes per 16-token subtile count MI: (weight subtiles
-// per wave NJ, register ring depth D).  Measured on MI355X at 8192 ->
-// 28672 on packed weights: one subtile keeps a 2-deep ring (M 1: 39.9 us
+// Streaming-kernel shapes per 16-token subtile count MI on packed weights:
+// (weight subtiles per wave NJ, register ring depth D).  Row-major weights
+// keep (4, 2) and M <= 32 (their fragment loads split every 128-byte line
+// over two instructions and need the deeper ring: M 32 on a 1-deep ring
+// took 82 us against 60-67).  Measured on MI355X at 8192 -> 28672: one subtile keeps a 2-deep ring (M 1: 39.9 us
 // against 41.4 with 1); from two subtiles on a 1-deep ring wins, its
 // registers leaving room for more waves (M 32: 47.4 -> 42.9 us), and the
 // streaming kernel beats the 64 x 128 tiles up to M = 64 (M 33 / 48 / 49:
 // 47.3 / 51.4 / 57.6 us against 62.3 / 62.5 / 62.8).
 #ifndef FP8B_STREAM_MAX_M
-#define FP8B_STREAM_MAX_M 64
+#define FP8B_STREAM_MAX_M 64  // 32 or 64
 #endif
 #ifndef FP8B_DEC3
 #define FP8B_DEC3 4, 1
@@ -1073,11 +1075,13 @@ template <int MI, bool PK>
 static void launch_decode(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
                           const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
                           hipStream_t s) {
-  if (MI == 1)
+  if constexpr (!PK)  // row-major weights: two loads per 128-byte line, a 2-deep ring
+    launch_decode_nj<MI, PK, 4, 2>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+  else if constexpr (MI == 1)
     launch_decode_nj<1, PK, FP8B_DEC1>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
-  else if (MI == 2)
+  else if constexpr (MI == 2)
     launch_decode_nj<2, PK, FP8B_DEC2>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
-  else if (MI == 3)
+  else if constexpr (MI == 3)
     launch_decode_nj<3, PK, FP8B_DEC3>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
   else
     launch_decode_nj<4, PK, FP8B_DEC4>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
@@ -1101,16 +1105,20 @@ template <bool PK>
 static void launch_block_any(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
                              const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
                              hipStream_t s) {
-  // M <= 64: the streaming kernel (one to four 16-token subtiles)
+  // the streaming kernel for M <= 64 on packed weights (one to four 16-token
+  // subtiles), M <= 32 on row-major ones
   if (M <= 16)
     launch_decode<1, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
   else if (M <= 32)
     launch_decode<2, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
-  else if (FP8B_STREAM_MAX_M >= 48 && M <= 48)
-    launch_decode<3, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
-  else if (FP8B_STREAM_MAX_M >= 64 && M <= 64)
-    launch_decode<4, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
-  else if (M <= 128)
+  else if (PK && FP8B_STREAM_MAX_M >= 64 && M <= 64) {
+    if constexpr (PK) {
+      if (M <= 48)
+        launch_decode<3, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+      else
+        launch_decode<4, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+    }
+  } else if (M <= 128)
     launch_block<SmallMCfg, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
   else
     launch_block<BlockCfg, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);

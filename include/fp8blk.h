@@ -160,8 +160,11 @@ int fp8_weight_pack(const uint8_t *w, int64_t G, int64_t N, int64_t K,
 
 /*
  * fp8_block_gemm_packed -- fp8_block_gemm (same operation, same passages,
- * bit-identical output) with the weight codes in the packed layout of
- * fp8_weight_pack.  Arguments as for fp8_block_gemm, except:
+ * same tolerance) with the weight codes in the packed layout of
+ * fp8_weight_pack.  The output is bit-identical to fp8_block_gemm's for
+ * M <= 32 and M > 64; for 33 <= M <= 64 the packed path streams the
+ * weights while the row-major one runs tiles, so the fp32 sums are taken in
+ * another (fixed) order.  Arguments as for fp8_block_gemm, except:
  *
  *   w_packed  N*K bytes from fp8_weight_pack (G = 1), 16-byte aligned.
  *   N <= 2^25.
