@@ -102,7 +102,9 @@ FP8B_EXPORT int fp8_weight_pack(const uint8_t* w, int64_t G, int64_t N, int64_t 
   if (G < 1 || N <= 0 || K <= 0 || G > kMaxDim || N > kMaxPackedN || K > kMaxDim) return FP8B_EINVAL;
   if (N % 128 != 0 || K % 128 != 0 || ld_w < K) return FP8B_EINVAL;
   if (!aligned(w, 16) || ld_w % 16 != 0 || !aligned(w_packed, 16)) return FP8B_EALIGN;
-  if (G * N / 256 * (K / 16) >= INT32_MAX) return FP8B_EINVAL;
+  // one thread per 16-byte piece, G * N * K / 16 of them, in one grid
+  // dimension (the quotient form cannot overflow)
+  if (G > (int64_t)INT32_MAX * 256 / (N * (K / 16))) return FP8B_EINVAL;
   return fp8blk::launch_weight_pack(w, G, N, K, ld_w, w_packed, as_stream(stream));
 }
 

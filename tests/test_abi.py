@@ -192,6 +192,8 @@ def test_packed_validation(L):
     assert p(*bad) == -2
     bad = list(args); bad[2] = (1 << 25) + 128
     assert p(*bad) == -1                                                  # N > 2^25
+    bad = list(args); bad[1] = 1 << 29; bad[2] = 1 << 25; bad[3] = bad[4] = 1 << 29
+    assert p(*bad) == -1                                                  # G*N*K/16 pieces too many
     f = L.fp8_block_gemm_packed
     args = [GOOD, 256, GOOD, GOOD, GOOD, 16, 256, 256, GOOD, 256, 1, NULL]
     bad = list(args); bad[10] = 3
