@@ -38,6 +38,12 @@
 //    barrier per K step.
 //  * Tile order is remapped so that each XCD (8 per chip, each with its own
 //    L2) works on a contiguous, grouped patch of output tiles.
+//  * Weights may also come in a packed layout (1 KB chunks of 16 rows x 64
+//    codes, K outermost; see packed_woff): each wave load is one contiguous
+//    chunk, and weight-streaming launches read one advancing front of HBM.
+//  * Up to 64 tokens (decode, the short tails of MoE experts) the weights
+//    are streamed once through registers instead of being tiled through LDS
+//    (stream_rows), the K range split over the workgroup's four waves.
 #include <algorithm>
 #include <type_traits>
 
@@ -210,17 +216,6 @@ __device__ __forceinline__ bf16x8 cvt8(uint32_t lo, uint32_t hi, float scale) {
 struct Frag16 {
   bf16x8 k[4];
 };
-
-__device__ __forceinline__ Frag16 load_frag(const uint8_t* t, int r, int g, float s_lo, float s_hi) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(t + lds_off(r, g));
-  const uint4 hi = *reinterpret_cast<const uint4*>(t + lds_off(r, g + 4));
-  Frag16 f;
-  f.k[0] = cvt8(lo.x, lo.y, s_lo);
-  f.k[1] = cvt8(lo.z, lo.w, s_lo);
-  f.k[2] = cvt8(hi.x, hi.y, s_hi);
-  f.k[3] = cvt8(hi.z, hi.w, s_hi);
-  return f;
-}
 
 __device__ __forceinline__ v4f mfma_bf16(bf16x8 a, bf16x8 b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
