@@ -16,8 +16,9 @@ The same JSON line carries
   roofline      for the dominant kernel (the block GEMM), its average
                 launch duration measured with events on its stream;
                 and, under measured_ceilings, what torch's bf16 GEMM
-                (hipBLASLt) reaches on the same shape and a 1 GiB device copy
-                reaches on this GPU;
+                (hipBLASLt) reaches on the same shape, what the library's
+                MFMA-only loop reaches (bf16 16x16x32 and FP8 16x16x128),
+                and what a 1 GiB device copy reaches on this GPU;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same
                 workload (rank 0, one GPU only), on all host threads and on
                 one;
@@ -147,6 +148,25 @@ def timed_graph(torch, fn, iters):
     t = e0.elapsed_time(e1) / iters * 1e-3
     del g
     return t
+
+
+def mfma_loop_rates(torch, F, dev):
+    """TFLOP/s of the library's MFMA-only loop (fp8b_mfma_loop): seeded
+    register operands, four waves per SIMD, ~0.3-0.6 ms per launch, timed
+    after the same settling as the step.  bf16 16x16x32 is the instruction
+    the GEMMs' products run on; FP8 16x16x128 is shown beside it."""
+    g = torch.Generator().manual_seed(5)
+    ops = {"bf16": torch.randn(64, 128, generator=g).to(torch.bfloat16).view(torch.int16).view(torch.int32),
+           "fp8": (torch.randn(64, 256, generator=g) * 4).to(torch.float8_e4m3fn).view(torch.uint8)
+           .view(torch.int32)}
+    wg = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(wg, 256, dtype=torch.float32, device=dev)
+    rates = {}
+    for name, kind, iters in (("bf16", F.MFMA_BF16_16X16X32, 8192), ("fp8", F.MFMA_FP8_16X16X128, 2048)):
+        w = ops[name].contiguous().to(dev)
+        t = timed(torch, lambda w=w, kind=kind, iters=iters: F.fp8b_mfma_loop(kind, w, iters, wg, out), 20)
+        rates[name] = wg * 4 * iters * 2 * F.MFMA_LOOP_FLOPS[kind] / t / 1e12
+    return rates
 
 
 def main():
@@ -282,8 +302,12 @@ def main():
         torch.cuda.empty_cache()
         copy_gbs = 2.0 * (1 << 30) / t_cp / 1e9
         mm_tflops = flops / t_mm / 1e12
+        loops = mfma_loop_rates(torch, F, dev)
         ceilings = {"bf16_gemm_torch_us": round(t_mm * 1e6, 2), "bf16_gemm_torch_TFLOPs": round(mm_tflops, 1),
                     "block_gemm_vs_bf16_gemm_torch": round(achieved / mm_tflops, 4),
+                    "mfma_loop_bf16_16x16x32_TFLOPs": round(loops["bf16"], 1),
+                    "mfma_loop_fp8_16x16x128_TFLOPs": round(loops["fp8"], 1),
+                    "block_gemm_vs_mfma_loop_bf16": round(achieved / loops["bf16"], 4),
                     "device_copy_GBps": round(copy_gbs, 1),
                     "act_quant_vs_device_copy": round(aq_bytes / t_aq / 1e9 / copy_gbs, 4)}
         roofline["measured_ceilings"] = ceilings

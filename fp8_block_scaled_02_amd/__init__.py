@@ -24,6 +24,8 @@ FP8B_OK = 0
 SCALE_FP32, SCALE_UE8M0, SCALE_E8M0_BYTE = 0, 1, 2
 OUT_F32, OUT_BF16 = 0, 1
 FMT_E4M3, FMT_E5M2 = 0, 1
+MFMA_BF16_16X16X32, MFMA_FP8_16X16X128 = 0, 1
+MFMA_LOOP_FLOPS = {MFMA_BF16_16X16X32: 16384, MFMA_FP8_16X16X128: 65536}   # per MFMA instruction
 DELAYED_HEADER_BYTES = 128 + 128 * 16    # FP8B_DELAYED_HEADER_BYTES of include/fp8blk.h
 
 _SCALE_FMT = {"fp32": SCALE_FP32, "ue8m0": SCALE_UE8M0, "e8m0": SCALE_E8M0_BYTE}
@@ -83,6 +85,8 @@ def lib():
         L.fp8_delayed_quant.argtypes = [vp, i64, vp, i64, ci, ctypes.c_float, vp, vp, vp]
         L.fp8_cast_f32.restype = ci
         L.fp8_cast_f32.argtypes = [vp, i64, ci, vp, vp]
+        L.fp8b_mfma_loop.restype = ci
+        L.fp8b_mfma_loop.argtypes = [ci, vp, i64, i64, vp, vp]
         _lib = L
     return _lib
 
@@ -378,3 +382,19 @@ def linear(x: torch.Tensor, w_q, w_scales, scale_fmt="fp32", out_dtype=torch.bfl
         raise ValueError("the block GEMM takes fp32 or ue8m0 (fp32-stored) scales")
     gemm = fp8_block_gemm_packed if packed else fp8_block_gemm
     return gemm(a, sa, w_q, w_scales, out_dtype)
+
+
+def fp8b_mfma_loop(kind: int, ops: torch.Tensor, iters: int, workgroups: int, out=None):
+    """The MFMA-only measurement loop (a measurement aid, not a step of the
+    method): ops is int32/uint32-sized [64, 64] operand words on the device;
+    returns out, float32 [workgroups, 256].  FLOPs of one call:
+    workgroups * 4 * iters * 2 * MFMA_LOOP_FLOPS[kind]."""
+    _need(ops.is_cuda and ops.element_size() == 4 and ops.numel() == 64 * 64 and ops.is_contiguous(),
+          "ops must be 64 x 64 contiguous 4-byte words on the GPU")
+    if out is None:
+        out = torch.empty(workgroups, 256, dtype=torch.float32, device=ops.device)
+    _need(out.dtype == torch.float32 and out.numel() >= workgroups * 256 and out.is_contiguous(),
+          "out must hold workgroups * 256 contiguous float32")
+    rc = lib().fp8b_mfma_loop(int(kind), _p(ops), int(iters), int(workgroups), _p(out), _stream(ops))
+    _check("fp8b_mfma_loop", rc)
+    return out

@@ -230,4 +230,14 @@ FP8B_EXPORT int fp8_cast_f32(const float* x, int64_t n, int fmt, uint8_t* q, voi
   return fp8blk::launch_cast(x, n, fmt, q, as_stream(stream));
 }
 
+FP8B_EXPORT int fp8b_mfma_loop(int kind, const uint32_t* ops, int64_t iters, int64_t workgroups, float* out,
+                               void* stream) {
+  if (kind != FP8B_MFMA_BF16_16X16X32 && kind != FP8B_MFMA_FP8_16X16X128) return FP8B_EUNSUPPORTED;
+  if (!ops || !out) return FP8B_EINVAL;
+  if (iters < 1 || iters > ((int64_t)1 << 30) || workgroups < 1 || workgroups > ((int64_t)1 << 20))
+    return FP8B_EINVAL;
+  if (!aligned(ops, 16) || !aligned(out, 4)) return FP8B_EALIGN;
+  return fp8blk::launch_mfma_loop(kind, ops, iters, workgroups, out, as_stream(stream));
+}
+
 }  // extern "C"

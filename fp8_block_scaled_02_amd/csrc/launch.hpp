@@ -36,6 +36,8 @@ int launch_block_gemm(const uint8_t* a, int64_t lda, const float* sa, const uint
 int launch_mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* ea, const uint8_t* b,
                    int64_t ldb, const uint8_t* eb, int64_t M, int64_t N, int64_t K, float* y,
                    int64_t ldy, hipStream_t s);
+int launch_mfma_loop(int kind, const uint32_t* ops, int64_t iters, int64_t workgroups, float* out,
+                     hipStream_t s);
 int launch_grouped_gemm(const uint8_t* a, const float* sa, int64_t T, const int32_t* row_index,
                         const int32_t* offs, int64_t R, int64_t E, const uint8_t* w,
                         const float* sw, int64_t N, int64_t K, void* y, int out_bf16,

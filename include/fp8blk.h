@@ -385,6 +385,37 @@ int fp8_delayed_quant(const void *x, int64_t n, void *state,
  */
 int fp8_cast_f32(const float *x, int64_t n, int fmt, uint8_t *q, void *stream);
 
+/*
+ * fp8b_mfma_loop -- a measurement aid, not a step of the method: a dense
+ * loop of one MFMA instruction on operands held in registers, with no
+ * memory traffic, conversion or rescale.  Its rate is the matrix-core
+ * ceiling the part sustains for that instruction, clock and power limits
+ * included; benchmarks set the GEMMs' rates beside it.
+ *
+ *   kind        FP8B_MFMA_BF16_16X16X32: v_mfma_f32_16x16x32_bf16, the
+ *               instruction every GEMM of this library runs its products
+ *               on; FP8B_MFMA_FP8_16X16X128: v_mfma_scale_f32_16x16x128_f8f6f4
+ *               on E4M3 operands with unit scales.
+ *   ops         uint32 [64][64], device, 16-byte aligned: row l is lane l's
+ *               operand words (bf16 pairs for kind 0, E4M3 bytes for kind
+ *               1), the same for every wave.  Chain c (0 or 1) takes A from
+ *               words 8c..8c+3 and B from 8c+4..8c+7 (kind 0), or A from
+ *               16c..16c+7 and B from 16c+8..16c+15 (kind 1); the other
+ *               words are not read.
+ *   iters       rounds per wave, 1 .. 2^30; a round is one MFMA on each of
+ *               the 2 chains, each accumulating into its own registers.
+ *   workgroups  1 .. 2^20 workgroups of 4 waves (256 threads).
+ *   out         float [workgroups][256], device, 4-byte aligned: each lane's
+ *               sum of its 8 accumulator values.
+ *
+ * FLOPs per call: workgroups * 4 * iters * 2 * 16384 (kind 0) or * 65536
+ * (kind 1).  Returns FP8B_EUNSUPPORTED for another kind.
+ */
+typedef enum { FP8B_MFMA_BF16_16X16X32 = 0, FP8B_MFMA_FP8_16X16X128 = 1 } fp8b_mfma_kind;
+
+int fp8b_mfma_loop(int kind, const uint32_t *ops, int64_t iters, int64_t workgroups,
+                   float *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
