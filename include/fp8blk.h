@@ -189,7 +189,15 @@ int fp8_block_gemm_packed(const uint8_t *a, int64_t ld_a,
  *           aligned (fp8_act_quant with block 32, FP8B_SCALE_E8M0_BYTE).
  *   M >= 0; N, K > 0 and multiples of 128; ld_a, ld_b < 2^24.
  *   y       float [M][ld_y], 16-byte aligned, ld_y % 4 == 0, ld_y >= N.
- *   Scale byte 0xFF (NaN) gives unspecified outputs.
+ *
+ * Each scale is folded into the exact FP8 -> bf16 widening of its block's
+ * codes, which keeps every widened code a normal bf16 for scale bytes 10 to
+ * 246; there y meets the fp32 tolerance of the other GEMMs.  fp8_act_quant
+ * gives bytes outside that range only to blocks whose amax is at most
+ * 448 * 2^-118 (about 2^-109.2) or above 448 * 2^119 (about 2^127.8): such
+ * a block's codes are rounded to bf16 subnormals (bytes below 10) or may
+ * overflow (bytes above 246).  Scale byte 0xFF (NaN) gives unspecified
+ * outputs.
  */
 int mxfp8_gemm(const uint8_t *a, int64_t ld_a, const uint8_t *a_e8m0,
                const uint8_t *b, int64_t ld_b, const uint8_t *b_e8m0,

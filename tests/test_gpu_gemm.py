@@ -283,6 +283,36 @@ def test_mx_gemm_applies_block_exponents_exactly(F, orc):
     np.testing.assert_array_equal(_np(y), want)
 
 
+
+@pytest.mark.parametrize("edge", ["low", "high"])
+def test_mx_gemm_exact_at_the_scale_byte_range_edges(F, orc, edge):
+    """Folding 2^(e - 127) into the widened codes keeps every code a normal
+    bf16 for scale bytes 10..246.  One operand takes bytes at an edge of that
+    range, the other bytes that keep every product and sum in fp32's normal
+    range; checked with each operand in each role."""
+    rng = np.random.default_rng(21 if edge == "low" else 22)
+    M = N = 128
+    K = 256
+
+    def codes(rows):
+        c = rng.integers(0, 0x7F, size=(rows, K)).astype(np.uint8)   # 0x7F is NaN
+        return c | (rng.integers(0, 2, size=(rows, K)).astype(np.uint8) << 7)
+
+    a, b = codes(M), codes(N)
+    if edge == "low":     # 2^-117 * 2^-9 = 2^-126; sums 146..152: products >= 2^-126
+        ea = rng.integers(10, 13, size=(M, K // 32)).astype(np.uint8)
+        eb = rng.integers(136, 141, size=(N, K // 32)).astype(np.uint8)
+    else:                 # 448 * 2^119 < bf16 max; sums <= 346: |y| < 2^118
+        ea = rng.integers(244, 247, size=(M, K // 32)).astype(np.uint8)
+        eb = rng.integers(96, 101, size=(N, K // 32)).astype(np.uint8)
+    for x, ex, w, ew in ((a, ea, b, eb), (b, eb, a, ea)):
+        y = F.mxfp8_gemm(*[torch.from_numpy(v).to(DEV) for v in (x, ex, w, ew)])
+        torch.cuda.synchronize()
+        yr, bnd = orc.mx_gemm(x, ex, w, ew)
+        assert np.all(np.isfinite(yr)) and np.all(bnd > 0)
+        assert_parity(_np(y), yr, bnd, False, f"mx scale bytes at the {edge} edge")
+
+
 # ---- MoE combine ---------------------------------------------------------------
 def _combine_check(F, orc, y, tr, gates, out_dtype, what):
     out = F.fp8_moe_combine(y, tr, gates, out_dtype)
