@@ -119,7 +119,13 @@ int fp8_weight_quant(const void *w, int64_t N, int64_t K, int64_t ld_w,
  *   y[m][n] = sum_kb a_scales[m][kb] * w_scales[n/128][kb] *
  *             sum_{k in block kb} value(a[m][k]) * value(w[n][k])
  *   with fp32 accumulation and a per-128-K-block rescale; y is written as
- *   fp32 or bf16 (round to nearest even).
+ *   fp32 or bf16 (round to nearest even).  The rescale multiplies each
+ *   block's fp32 partial sum by the fp32 product a_scales * w_scales: y
+ *   meets the stated tolerance while that product is a normal fp32 number
+ *   (at least 2^-126) and y is finite; a smaller product carries fp32's
+ *   subnormal rounding (with fp8_act_quant scales, only for blocks whose
+ *   activation and weight amax are both tiny).  The same holds for the
+ *   packed and grouped variants below.
  *
  *   a         codes [M][ld_a], 16-byte aligned, ld_a % 16 == 0, >= K.
  *   a_scales  float [M][K/128], contiguous (fp8_act_quant with block 128).

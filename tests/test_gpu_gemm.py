@@ -83,6 +83,36 @@ def test_block_gemm_ue8m0_small(F, orc):
     assert_parity(yg, yr, bnd, True, "ue8m0 128x512x1024")
 
 
+@pytest.mark.parametrize("M", [1, 40, 100, 300])
+@pytest.mark.parametrize("scale", ["small", "large"])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_block_gemm_scale_products_near_the_fp32_range_ends(F, orc, M, scale, out):
+    """Hand-made codes and scales whose per-block products a_scales * w_scales
+    lie just above fp32's smallest normal (2^-126 .. 2^-122) or near 2^100,
+    on every path (streaming for M <= 64, 64- and 128-row tiles) and both
+    weight layouts."""
+    rng = np.random.default_rng(31 + M)
+    N, K = 256, 256
+
+    def codes(rows):
+        c = rng.integers(0, 0x7F, size=(rows, K)).astype(np.uint8)   # 0x7F is NaN
+        return c | (rng.integers(0, 2, size=(rows, K)).astype(np.uint8) << 7)
+
+    a, w = codes(M), codes(N)
+    lo_a, lo_w = (-66, -60) if scale == "small" else (50, 49)
+    sa = np.ldexp(rng.uniform(1, 2, size=(M, K // 128)), lo_a).astype(np.float32)
+    sw = np.ldexp(rng.uniform(1, 2, size=(N // 128, K // 128)), lo_w).astype(np.float32)
+    prod = sa[:, None, :].astype(np.float64) * sw[None, :, :]
+    assert prod.min() >= 2.0 ** -126 and prod.max() < 2.0 ** 102
+    yr, bnd = orc.block_gemm(a, sa, w, sw)
+    assert np.all(np.isfinite(yr)) and bnd.max() < 2.0 ** 127
+    ta, tsa, tw, tsw = (torch.from_numpy(v).to(DEV) for v in (a, sa, w, sw))
+    for y in (F.fp8_block_gemm(ta, tsa, tw, tsw, out),
+              F.fp8_block_gemm_packed(ta, tsa, F.fp8_weight_pack(tw), tsw, out)):
+        torch.cuda.synchronize()
+        assert_parity(_np(y), yr, bnd, out == torch.bfloat16, f"scale products {scale}, M {M}")
+
+
 def test_block_gemm_decode_full(F, orc):
     c = W.decode_linear(device=DEV)
     a, sa = F.fp8_act_quant(c.x, 128, "ue8m0")
