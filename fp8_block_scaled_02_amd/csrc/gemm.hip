@@ -681,9 +681,10 @@ constexpr int stream_part_bytes() {
 // the lines into its MFMA fragment through a private LDS tile in lds_a,
 // 4 * MI * 2048 bytes per workgroup); sarow[i]: the per-block scales of
 // this lane's row 16i + l16; wload(j, kb): this lane's fragment of weight
-// subtile j at K block kb; swrow: the weight-scale row of these rows.  Every wave of the workgroup must call it; the sums are complete
-// in wave 0 only (the return value says which), and `part` may be reused by
-// the caller only after a barrier.
+// subtile j at K block kb; swrow: the weight-scale row of these rows.
+// Every wave of the workgroup must call it; the sums are complete in wave 0
+// only (the return value says which), and `part` may be reused by the
+// caller only after a barrier.
 template <int MI, int NJ = kStreamNJ, int D = kStreamDepth, class WLoad>
 __device__ __forceinline__ bool stream_rows(const uint8_t* const (&aline)[MI][2], const float* const (&sarow)[MI],
                                             WLoad wload, const float* swrow, int nkb, uint8_t* lds_a,
@@ -1050,11 +1051,13 @@ static int cu_count() {
 // (weight subtiles per wave NJ, register ring depth D).  Row-major weights
 // keep (4, 2) and M <= 32 (their fragment loads split every 128-byte line
 // over two instructions and need the deeper ring: M 32 on a 1-deep ring
-// took 82 us against 60-67).  Measured on MI355X at 8192 -> 28672: one subtile keeps a 2-deep ring (M 1: 39.9 us
-// against 41.4 with 1); from two subtiles on a 1-deep ring wins, its
-// registers leaving room for more waves (M 32: 47.4 -> 42.9 us), and the
-// streaming kernel beats the 64 x 128 tiles up to M = 64 (M 33 / 48 / 49:
-// 47.3 / 51.4 / 57.6 us against 62.3 / 62.5 / 62.8).
+// took 82 us against 60-67).  Measured on MI355X at 8192 -> 28672: one
+// subtile keeps a 2-deep ring (M 1: 39.9 us against 41.4 with 1); from two
+// subtiles on a 1-deep ring wins, its registers leaving room for more waves
+// (M 32: 47.4 -> 42.9 us), and the streaming kernel beats the 64 x 128
+// tiles up to M = 64 (M 33 / 48 / 49: 47.3 / 51.4 / 57.6 us against 62.3 /
+// 62.5 / 62.8).  A sweep of NJ in {2, 4, 8} and D in {1, 2, 3} for one and
+// two subtiles found nothing faster than these.
 #ifndef FP8B_STREAM_MAX_M
 #define FP8B_STREAM_MAX_M 64  // 32 or 64
 #endif
