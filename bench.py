@@ -36,6 +36,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -66,12 +67,21 @@ def parse():
     return p.parse_args()
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed, so that
+    editing a comment does not count as changing a kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_hash():
+    """Hash of the kernel sources' code (comments and layout ignored)."""
     h = hashlib.sha256()
     csrc = os.path.join(HERE, "fp8_block_scaled_02_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

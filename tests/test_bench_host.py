@@ -44,3 +44,16 @@ def test_traffic_is_read_only_for_the_current_sources(profile_dir):
     f.write_text("kernel_hash: %s\n" % cur)
     assert bench.load_traffic("k") is None          # no figure
     assert bench.load_traffic("missing") is None
+
+
+def test_kernel_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    csrc = tmp_path / "fp8_block_scaled_02_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (csrc / "k.hip").write_text("// a kernel\n__global__ void k(int* p) { p[0] = 1; }\n")
+    monkeypatch.setattr(bench, "HERE", str(tmp_path))
+    h0 = bench.kernel_hash()
+    (csrc / "k.hip").write_text("// the kernel, reworded\n/* and a block\n comment */\n"
+                                "__global__ void k(int* p) {   p[0] = 1;  }  // trailing\n")
+    assert bench.kernel_hash() == h0
+    (csrc / "k.hip").write_text("// a kernel\n__global__ void k(int* p) { p[0] = 2; }\n")
+    assert bench.kernel_hash() != h0
