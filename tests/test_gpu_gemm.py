@@ -260,6 +260,35 @@ def test_grouped_every_tail_kind(F, orc):
     assert_parity(yg, yr, bnd, True, "moe tails")
 
 
+@pytest.mark.parametrize("scale", ["small", "large"])
+def test_grouped_scale_products_near_the_fp32_range_ends(F, orc, scale):
+    """The grouped GEMM with hand-made codes and scale products just above
+    2^-126 or near 2^100: experts of 5 rows (streaming items), 40 (a padded
+    tile) and 150 (a whole tile and a streaming tail), both weight layouts."""
+    rng = np.random.default_rng(51)
+    T, E, N, K = 120, 3, 256, 256
+    counts = [5, 40, 150]
+
+    def codes(*shape):
+        c = rng.integers(0, 0x7F, size=shape).astype(np.uint8)      # 0x7F is NaN
+        return c | (rng.integers(0, 2, size=shape).astype(np.uint8) << 7)
+
+    a, w = codes(T, K), codes(E, N, K)
+    lo_a, lo_w = (-66, -60) if scale == "small" else (50, 49)
+    sa = np.ldexp(rng.uniform(1, 2, size=(T, K // 128)), lo_a).astype(np.float32)
+    sw = np.ldexp(rng.uniform(1, 2, size=(E, N // 128, K // 128)), lo_w).astype(np.float32)
+    ri = rng.integers(0, T, size=sum(counts)).astype(np.int32)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    yr, bnd = orc.grouped_gemm(a, sa, ri, offs, list(w), list(sw))
+    assert np.all(np.isfinite(yr)) and bnd.max() < 2.0 ** 127
+    ta, tsa, tw, tsw, tri, tof = (torch.from_numpy(v).to(DEV) for v in (a, sa, w, sw, ri, offs))
+    for out in (torch.float32, torch.bfloat16):
+        for y in (F.fp8_grouped_gemm(ta, tsa, tri, tof, tw, tsw, out),
+                  F.fp8_grouped_gemm_packed(ta, tsa, tri, tof, F.fp8_weight_pack(tw), tsw, out)):
+            torch.cuda.synchronize()
+            assert_parity(_np(y), yr, bnd, out == torch.bfloat16, f"grouped, scale products {scale}")
+
+
 def test_grouped_only_short_experts(F, orc):
     """Every expert below 32 rows: no tile items at all."""
     counts = [3, 0, 31, 7, 1, 0, 20, 16]
