@@ -113,6 +113,43 @@ def test_block_gemm_scale_products_near_the_fp32_range_ends(F, orc, M, scale, ou
         assert_parity(_np(y), yr, bnd, out == torch.bfloat16, f"scale products {scale}, M {M}")
 
 
+@pytest.mark.parametrize("M", [40, 300])
+def test_linear_step_graph_replay_matches_eager(F, M):
+    """act_quant + block GEMM (packed weights) captured once as a HIP graph
+    and replayed on new activations, with eager work between replays: every
+    replay equals the eager step bit for bit (no allocation, memset or
+    synchronisation is recorded)."""
+    N, K = 384, 640
+    g = torch.Generator(device=DEV).manual_seed(61 + M)
+    w = (torch.randn(N, K, device=DEV, generator=g) * 0.02).to(torch.bfloat16)
+    wq, ws = F.fp8_weight_quant(w, "fp32")
+    wp = F.fp8_weight_pack(wq)
+    x = torch.empty(M, K, dtype=torch.bfloat16, device=DEV)
+    a = torch.empty(M, K, dtype=torch.uint8, device=DEV)
+    sa = torch.empty(M, K // 128, dtype=torch.float32, device=DEV)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        F.fp8_act_quant(x, 128, "fp32", q=a, scales=sa)
+        F.fp8_block_gemm_packed(a, sa, wp, ws, torch.bfloat16, y=y)
+
+    x.copy_(torch.randn(M, K, device=DEV, generator=g).to(torch.bfloat16))
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(3):
+        x.copy_((torch.randn(M, K, device=DEV, generator=g) * (1 + r)).to(torch.bfloat16))
+        step()
+        torch.cuda.synchronize()
+        want = y.clone()
+        y.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), want.view(torch.int16)), f"replay {r}"
+
+
 def test_block_gemm_decode_full(F, orc):
     c = W.decode_linear(device=DEV)
     a, sa = F.fp8_act_quant(c.x, 128, "ue8m0")
