@@ -295,6 +295,30 @@ def test_kv_dequant_every_code_and_strides(F, orc):
     _deq_check(o[:, :512], orc.kv_dequant(q, s), "kv dequant codes")
 
 
+
+@pytest.mark.parametrize("T,D", [(77, 16), (9, 16384), (100, 1040), (3, 2048)])
+def test_kv_dequant_row_grouping(F, orc, T, D):
+    """Every branch of the dequant grid: many rows per workgroup with a
+    partial last one (16 codes a row), a row over two segments (16384), a
+    row whose 130 groups cannot share a workgroup, one row of 256 groups."""
+    rng = np.random.default_rng(T * 7 + D)
+    q = rng.integers(0, 256, size=(T, D), dtype=np.uint8)
+    s = np.exp(rng.uniform(-20, 20, size=T)).astype(np.float32)
+    out = F.fp8_kv_dequant(torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV))
+    torch.cuda.synchronize()
+    _deq_check(_np(out.view(torch.int16)).view(np.uint16), orc.kv_dequant(q, s), f"kv dequant {T}x{D}")
+
+
+def test_weight_dequant_two_segments(F, orc):
+    """A 16384-wide weight row spans two segments of the dequant grid."""
+    rng = np.random.default_rng(5)
+    q = rng.integers(0, 256, size=(256, 16384), dtype=np.uint8)
+    sc = np.exp(rng.uniform(-20, 20, size=(2, 128))).astype(np.float32)
+    out = F.fp8_weight_dequant(torch.from_numpy(q).to(DEV), torch.from_numpy(sc).to(DEV))
+    torch.cuda.synchronize()
+    _deq_check(_np(out.view(torch.int16)).view(np.uint16), orc.weight_dequant(q, sc), "weight dequant 256x16384")
+
+
 # ---- delayed scaling ----------------------------------------------------------
 def _delayed_steps(S, n, seed, dev="cpu"):
     g = W.gen(seed, dev)
