@@ -496,7 +496,7 @@ def run_legs(torch, F, W, dev, only=""):
         x = c.x
         n = x.numel()
         del c
-        ds = F.DelayedScaler(16, "max", 400.0, device=dev)
+        ds = F.DelayedScaler(128, "max", 400.0, device=dev)   # amax_history_len 128, algo max
         q = torch.empty(n, dtype=torch.uint8, device=dev)
         su = torch.empty(1, dtype=torch.float32, device=dev)
         t = timed_graph(torch, lambda: ds.quantize(x, q=q, scale_used=su), iters)

@@ -121,6 +121,20 @@ def _need(cond, msg):
         raise ValueError(msg)
 
 
+def _on_gpu(*ts):
+    """Every tensor is on the same GPU as the first: the kernels dereference
+    data_ptr() as device memory, so a host tensor (or one on another GPU)
+    must never reach them."""
+    dev = ts[0].device
+    for t in ts:
+        _need(t.is_cuda, f"every tensor must be on a GPU (found one on {t.device})")
+        _need(t.device == dev, f"every tensor must be on {dev} (found one on {t.device})")
+
+
+def _shape(t, shape, name):
+    _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+
+
 def fp8_act_quant(x: torch.Tensor, block_k: int = 128, scale_fmt="fp32", q=None, scales=None):
     """Dynamic per-token, per-block activation quantisation.
 
@@ -135,7 +149,13 @@ def fp8_act_quant(x: torch.Tensor, block_k: int = 128, scale_fmt="fp32", q=None,
     if scales is None:
         sdt = torch.uint8 if f == SCALE_E8M0_BYTE else torch.float32
         scales = torch.empty(M, max(K // block_k, 0), dtype=sdt, device=x.device)
-    _need(q.stride(1) == 1 and scales.is_contiguous(), "q rows and scales must be contiguous")
+    _need(q.dtype == torch.uint8 and q.dim() == 2 and q.stride(1) == 1, "q must be 2-D uint8, rows contiguous")
+    _shape(q, (M, K), "q")
+    _need(scales.dtype == (torch.uint8 if f == SCALE_E8M0_BYTE else torch.float32),
+          "scales must be uint8 for e8m0, float32 otherwise")
+    _need(scales.is_contiguous(), "scales must be contiguous")
+    _shape(scales, (M, K // block_k if block_k > 0 else 0), "scales")
+    _on_gpu(x, q, scales)
     rc = lib().fp8_act_quant(_p(x), M, K, x.stride(0) if M else K, block_k, f, _p(q),
                              q.stride(0) if M else K, _p(scales), _stream(x))
     _check("fp8_act_quant", rc)
@@ -151,6 +171,11 @@ def fp8_weight_quant(w: torch.Tensor, scale_fmt="fp32", q=None, scales=None):
         q = torch.empty(N, K, dtype=torch.uint8, device=w.device)
     if scales is None:
         scales = torch.empty(N // 128, K // 128, dtype=torch.float32, device=w.device)
+    _need(q.dtype == torch.uint8 and q.dim() == 2 and q.stride(1) == 1, "q must be 2-D uint8, rows contiguous")
+    _shape(q, (N, K), "q")
+    _need(scales.dtype == torch.float32 and scales.is_contiguous(), "scales must be contiguous float32")
+    _shape(scales, (N // 128, K // 128), "scales")
+    _on_gpu(w, q, scales)
     rc = lib().fp8_weight_quant(_p(w), N, K, w.stride(0), _fmt(scale_fmt), _p(q), q.stride(0),
                                 _p(scales), _stream(w))
     _check("fp8_weight_quant", rc)
@@ -165,7 +190,10 @@ def fp8_weight_dequant(q: torch.Tensor, scales: torch.Tensor, w=None):
     N, K = q.shape
     if w is None:
         w = torch.empty(N, K, dtype=torch.bfloat16, device=q.device)
-    _need(w.dtype == torch.bfloat16 and w.stride(1) == 1, "w must be bf16, rows contiguous")
+    _need(w.dtype == torch.bfloat16 and w.dim() == 2 and w.stride(1) == 1, "w must be 2-D bf16, rows contiguous")
+    _shape(scales, (N // 128, K // 128), "scales")
+    _shape(w, (N, K), "w")
+    _on_gpu(q, scales, w)
     rc = lib().fp8_weight_dequant(_p(q), N, K, q.stride(0), _p(scales), _p(w), w.stride(0), _stream(q))
     _check("fp8_weight_dequant", rc)
     return w
@@ -181,10 +209,13 @@ def fp8_moe_combine(y: torch.Tensor, token_rows: torch.Tensor, gates: torch.Tens
     _need(token_rows.shape == gates.shape and token_rows.dim() == 2, "token_rows and gates must be [T, k]")
     R, N = y.shape
     T, k = token_rows.shape
+    _need(out_dtype in (torch.bfloat16, torch.float32), "out_dtype must be bfloat16 or float32")
     od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
     if out is None:
         out = torch.empty(T, N, dtype=out_dtype, device=y.device)
     _need(out.is_contiguous() and out.dtype == out_dtype, "out must be contiguous of out_dtype")
+    _shape(out, (T, N), "out")
+    _on_gpu(y, token_rows, gates, out)
     rc = lib().fp8_moe_combine(_p(y), R, N, _p(token_rows), _p(gates), T, k, _p(out), od, _stream(y))
     _check("fp8_moe_combine", rc)
     return out
@@ -212,6 +243,11 @@ def fp8_kv_quant(x: torch.Tensor, q=None, scales=None):
         q = torch.empty(T, D, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(T, dtype=torch.float32, device=x.device)
+    _need(q.dtype == torch.uint8 and q.dim() == 2 and q.stride(1) == 1, "q must be 2-D uint8, rows contiguous")
+    _shape(q, (T, D), "q")
+    _need(scales.dtype == torch.float32 and scales.is_contiguous(), "scales must be contiguous float32")
+    _shape(scales, (T,), "scales")
+    _on_gpu(x, q, scales)
     rc = lib().fp8_kv_quant(_p(x), T, D, x.stride(0), _p(q), q.stride(0), _p(scales), _stream(x))
     _check("fp8_kv_quant", rc)
     return q, scales
@@ -224,6 +260,10 @@ def fp8_kv_dequant(q: torch.Tensor, scales: torch.Tensor, out=None):
     T, D = q.shape
     if out is None:
         out = torch.empty(T, D, dtype=torch.bfloat16, device=q.device)
+    _shape(scales, (T,), "scales")
+    _need(out.dtype == torch.bfloat16 and out.dim() == 2 and out.stride(1) == 1, "out must be 2-D bf16, rows contiguous")
+    _shape(out, (T, D), "out")
+    _on_gpu(q, scales, out)
     rc = lib().fp8_kv_dequant(_p(q), T, D, q.stride(0), _p(scales), _p(out), out.stride(0), _stream(q))
     _check("fp8_kv_dequant", rc)
     return out
@@ -245,6 +285,7 @@ class DelayedScaler:
         self.reset()
 
     def reset(self):
+        _on_gpu(self.state)
         rc = lib().fp8_delayed_state_init(_p(self.state), self.history_len, _stream(self.state))
         _check("fp8_delayed_state_init", rc)
 
@@ -254,23 +295,73 @@ class DelayedScaler:
             q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
         if scale_used is None:
             scale_used = torch.empty(1, dtype=torch.float32, device=x.device)
+        _need(q.dtype == torch.uint8 and q.is_contiguous() and q.numel() == x.numel(),
+              "q must be contiguous uint8 with one code per element of x")
+        _need(scale_used.dtype == torch.float32 and scale_used.numel() >= 1, "scale_used must be float32 [1]")
+        _on_gpu(x, self.state, q, scale_used)
         rc = lib().fp8_delayed_quant(_p(x), x.numel(), _p(self.state), self.history_len, self.algo,
                                      self.divisor, _p(q), _p(scale_used), _stream(x))
         _check("fp8_delayed_quant", rc)
         return q, scale_used
 
 
+def _codes(t, name):
+    _need(t.dtype == torch.uint8 and t.dim() == 2 and t.stride(1) == 1, f"{name} must be 2-D uint8 codes, rows contiguous")
+
+
+def _gemm_operands(a, a_scales, w, w_scales):
+    """Codes a [M, K] and w [N, K]; fp32 scales [M, K/128] and
+    [N/128, K/128], contiguous (the layouts the kernels index)."""
+    _codes(a, "a")
+    _codes(w, "w")
+    M, K = a.shape
+    N = w.shape[0]
+    _need(w.shape[1] == K, f"w must be [N, K] with K = {K}")
+    _need(a_scales.dtype == torch.float32 and w_scales.dtype == torch.float32, "scales must be float32")
+    _need(a_scales.is_contiguous() and w_scales.is_contiguous(), "scales must be contiguous")
+    _shape(a_scales, (M, K // 128), "a_scales")
+    _shape(w_scales, (N // 128, K // 128), "w_scales")
+
+
+def _gemm_output(y, rows, N, out_dtype):
+    _need(out_dtype in (torch.bfloat16, torch.float32), "out_dtype must be bfloat16 or float32")
+    _need(y.dtype == out_dtype and y.dim() == 2 and y.stride(1) == 1, f"y must be 2-D {out_dtype}, rows contiguous")
+    _shape(y, (rows, N), "y")
+
+
+def _grouped_operands(a, a_scales, row_index, expert_offsets, w, w_scales, out_dtype):
+    """Token codes a [T, K] and scales [T, K/128], routing int32 row_index [R]
+    and expert_offsets [E+1], expert weights [E, N, K] with scales
+    [E, N/128, K/128], all contiguous."""
+    _need(a.dtype == torch.uint8 and a.dim() == 2 and a.is_contiguous(), "a must be contiguous 2-D uint8 codes")
+    _need(w.dtype == torch.uint8 and w.dim() == 3 and w.is_contiguous(), "w must be contiguous uint8 [E, N, K]")
+    T, K = a.shape
+    E, N, Kw = w.shape
+    _need(Kw == K, f"w must be [E, N, K] with K = {K}")
+    _need(row_index.dtype == torch.int32 and expert_offsets.dtype == torch.int32, "routing must be int32")
+    _need(row_index.dim() == 1 and row_index.is_contiguous(), "row_index must be a contiguous 1-D tensor")
+    _need(expert_offsets.dim() == 1 and expert_offsets.is_contiguous(), "expert_offsets must be a contiguous 1-D tensor")
+    _need(expert_offsets.numel() == E + 1, f"expert_offsets must hold E + 1 = {E + 1} entries")
+    _need(a_scales.dtype == torch.float32 and a_scales.is_contiguous(), "a_scales must be contiguous float32")
+    _shape(a_scales, (T, K // 128), "a_scales")
+    _need(w_scales.dtype == torch.float32 and w_scales.is_contiguous(), "w_scales must be contiguous float32")
+    _shape(w_scales, (E, N // 128, K // 128), "w_scales")
+    _need(out_dtype in (torch.bfloat16, torch.float32), "out_dtype must be bfloat16 or float32")
+    od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    return T, row_index.shape[0], E, N, K, od
+
+
 def fp8_block_gemm(a, a_scales, w, w_scales, out_dtype=torch.bfloat16, y=None):
     """y[M, N] = block-scaled FP8 GEMM of codes a [M, K] and w [N, K] with
     fp32 scales a_scales [M, K/128] and w_scales [N/128, K/128]."""
-    _need(a.dtype == torch.uint8 and w.dtype == torch.uint8, "codes must be uint8")
-    _need(a_scales.dtype == torch.float32 and w_scales.dtype == torch.float32, "scales must be float32")
+    _gemm_operands(a, a_scales, w, w_scales)
     M, K = a.shape
     N = w.shape[0]
     od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
     if y is None:
         y = torch.empty(M, N, dtype=out_dtype, device=a.device)
-    _need(y.stride(1) == 1, "y rows must be contiguous")
+    _gemm_output(y, M, N, out_dtype)
+    _on_gpu(a, a_scales, w, w_scales, y)
     rc = lib().fp8_block_gemm(_p(a), a.stride(0) if M else K, _p(a_scales), _p(w), w.stride(0),
                               _p(w_scales), M, N, K, _p(y), y.stride(0) if M else N, od, _stream(a))
     _check("fp8_block_gemm", rc)
@@ -290,7 +381,9 @@ def fp8_weight_pack(w: torch.Tensor, out=None):
     _need(w.dim() == 2 or G == 1 or w.stride(0) == N * ld, "matrices of w must be [N][ld] one after another")
     if out is None:
         out = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
-    _need(out.is_contiguous() and out.numel() == G * N * K, "out must be contiguous with G*N*K bytes")
+    _need(out.dtype == torch.uint8 and out.is_contiguous() and out.numel() == G * N * K,
+          "out must be contiguous uint8 with G*N*K bytes")
+    _on_gpu(w, out)
     rc = lib().fp8_weight_pack(_p(w), G, N, K, ld, _p(out), _stream(w))
     _check("fp8_weight_pack", rc)
     return out
@@ -298,16 +391,15 @@ def fp8_weight_pack(w: torch.Tensor, out=None):
 
 def fp8_block_gemm_packed(a, a_scales, w_packed, w_scales, out_dtype=torch.bfloat16, y=None):
     """fp8_block_gemm with the weight codes from fp8_weight_pack (shape [N, K])."""
-    _need(a.dtype == torch.uint8 and w_packed.dtype == torch.uint8, "codes must be uint8")
-    _need(a_scales.dtype == torch.float32 and w_scales.dtype == torch.float32, "scales must be float32")
-    _need(w_packed.is_contiguous() and w_packed.dim() == 2, "w_packed must be a contiguous [N, K] tensor")
+    _need(w_packed.dim() == 2 and w_packed.is_contiguous(), "w_packed must be a contiguous [N, K] tensor")
+    _gemm_operands(a, a_scales, w_packed, w_scales)
     M, K = a.shape
     N = w_packed.shape[0]
-    _need(w_packed.shape[1] == K, "w_packed must be [N, K]")
     od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
     if y is None:
         y = torch.empty(M, N, dtype=out_dtype, device=a.device)
-    _need(y.stride(1) == 1, "y rows must be contiguous")
+    _gemm_output(y, M, N, out_dtype)
+    _on_gpu(a, a_scales, w_packed, w_scales, y)
     rc = lib().fp8_block_gemm_packed(_p(a), a.stride(0) if M else K, _p(a_scales), _p(w_packed), _p(w_scales),
                                      M, N, K, _p(y), y.stride(0) if M else N, od, _stream(a))
     _check("fp8_block_gemm_packed", rc)
@@ -317,11 +409,18 @@ def fp8_block_gemm_packed(a, a_scales, w_packed, w_scales, out_dtype=torch.bfloa
 def mxfp8_gemm(a, a_e8m0, b, b_e8m0, y=None):
     """y[M, N] (fp32) = MXFP8 GEMM of codes a [M, K], b [N, K] with E8M0
     bytes a_e8m0 [M, K/32], b_e8m0 [N, K/32]."""
-    _need(a_e8m0.dtype == torch.uint8 and b_e8m0.dtype == torch.uint8, "E8M0 scales must be uint8")
+    _codes(a, "a")
+    _codes(b, "b")
     M, K = a.shape
     N = b.shape[0]
+    _need(b.shape[1] == K, f"b must be [N, K] with K = {K}")
+    for t, rows, name in ((a_e8m0, M, "a_e8m0"), (b_e8m0, N, "b_e8m0")):
+        _need(t.dtype == torch.uint8 and t.is_contiguous(), f"{name} must be contiguous uint8 E8M0 bytes")
+        _shape(t, (rows, K // 32), name)
     if y is None:
         y = torch.empty(M, N, dtype=torch.float32, device=a.device)
+    _gemm_output(y, M, N, torch.float32)
+    _on_gpu(a, a_e8m0, b, b_e8m0, y)
     rc = lib().mxfp8_gemm(_p(a), a.stride(0) if M else K, _p(a_e8m0), _p(b), b.stride(0), _p(b_e8m0),
                           M, N, K, _p(y), y.stride(0) if M else N, _stream(a))
     _check("mxfp8_gemm", rc)
@@ -332,14 +431,12 @@ def fp8_grouped_gemm(a, a_scales, row_index, expert_offsets, w, w_scales, out_dt
     """Grouped MoE GEMM: a [T, K] token codes, a_scales [T, K/128],
     row_index int32 [R], expert_offsets int32 [E+1] (device), w [E, N, K],
     w_scales [E, N/128, K/128] -> y [R, N] in routed order."""
-    _need(row_index.dtype == torch.int32 and expert_offsets.dtype == torch.int32, "routing must be int32")
-    _need(a.is_contiguous() and w.is_contiguous(), "a and w must be contiguous")
-    T, K = a.shape
-    E, N, _ = w.shape
-    R = row_index.shape[0]
-    od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    T, R, E, N, K, od = _grouped_operands(a, a_scales, row_index, expert_offsets, w, w_scales, out_dtype)
     if y is None:
         y = torch.empty(R, N, dtype=out_dtype, device=a.device)
+    _need(y.is_contiguous(), "y must be contiguous")
+    _gemm_output(y, R, N, out_dtype)
+    _on_gpu(a, a_scales, row_index, expert_offsets, w, w_scales, y)
     rc = lib().fp8_grouped_gemm(_p(a), _p(a_scales), T, _p(row_index), _p(expert_offsets), R, E,
                                 _p(w), _p(w_scales), N, K, _p(y), od, _stream(a))
     _check("fp8_grouped_gemm", rc)
@@ -349,15 +446,12 @@ def fp8_grouped_gemm(a, a_scales, row_index, expert_offsets, w, w_scales, out_dt
 def fp8_grouped_gemm_packed(a, a_scales, row_index, expert_offsets, w_packed, w_scales, out_dtype=torch.bfloat16,
                             y=None):
     """fp8_grouped_gemm with the expert weights from fp8_weight_pack (shape [E, N, K])."""
-    _need(row_index.dtype == torch.int32 and expert_offsets.dtype == torch.int32, "routing must be int32")
-    _need(a.is_contiguous() and w_packed.is_contiguous() and w_packed.dim() == 3,
-          "a and w_packed must be contiguous, w_packed [E, N, K]")
-    T, K = a.shape
-    E, N, _ = w_packed.shape
-    R = row_index.shape[0]
-    od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    T, R, E, N, K, od = _grouped_operands(a, a_scales, row_index, expert_offsets, w_packed, w_scales, out_dtype)
     if y is None:
         y = torch.empty(R, N, dtype=out_dtype, device=a.device)
+    _need(y.is_contiguous(), "y must be contiguous")
+    _gemm_output(y, R, N, out_dtype)
+    _on_gpu(a, a_scales, row_index, expert_offsets, w_packed, w_scales, y)
     rc = lib().fp8_grouped_gemm_packed(_p(a), _p(a_scales), T, _p(row_index), _p(expert_offsets), R, E,
                                        _p(w_packed), _p(w_scales), N, K, _p(y), od, _stream(a))
     _check("fp8_grouped_gemm_packed", rc)
@@ -369,6 +463,9 @@ def fp8_cast_f32(x: torch.Tensor, fmt=FMT_E4M3, q=None):
     _need(x.dtype == torch.float32 and x.is_contiguous(), "x must be contiguous float32")
     if q is None:
         q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _need(q.dtype == torch.uint8 and q.is_contiguous() and q.numel() == x.numel(),
+          "q must be contiguous uint8 with one code per element of x")
+    _on_gpu(x, q)
     rc = lib().fp8_cast_f32(_p(x), x.numel(), int(fmt), _p(q), _stream(x))
     _check("fp8_cast_f32", rc)
     return q
@@ -395,6 +492,7 @@ def fp8b_mfma_loop(kind: int, ops: torch.Tensor, iters: int, workgroups: int, ou
         out = torch.empty(workgroups, 256, dtype=torch.float32, device=ops.device)
     _need(out.dtype == torch.float32 and out.numel() >= workgroups * 256 and out.is_contiguous(),
           "out must hold workgroups * 256 contiguous float32")
+    _on_gpu(ops, out)
     rc = lib().fp8b_mfma_loop(int(kind), _p(ops), int(iters), int(workgroups), _p(out), _stream(ops))
     _check("fp8b_mfma_loop", rc)
     return out

@@ -349,6 +349,36 @@ def test_delayed_scaling_steps(F, orc, L, algo):
     assert _np(su)[0] == 1.0 and (_np(q) == q2[0]).all()
 
 
+@pytest.mark.parametrize("algo", ["max", "latest"])
+def test_delayed_scaling_history_128(F, orc, algo):
+    """The pitfall section's setting, amax_history_len = 128 with the max
+    algorithm (and latest beside it), over 150 steps: the history fills past
+    64 entries (the closing wave's strided scan takes a second pass) and then
+    wraps.  Step magnitudes fall steadily, so once the window is full every
+    step's window maximum is its oldest entry and changes as that entry
+    leaves; an all-zero step and a late spike sit inside the run."""
+    S, n, L = 150, 8192, 128
+    g = W.gen(128 + (algo == "max"))
+    mag = torch.exp2(torch.linspace(6.0, -6.0, S)).reshape(S, 1)
+    mag[140] = 2.0 ** 8                                   # a late spike (still in the window at the end)
+    x = (torch.randn(S, n, generator=g) * mag).to(torch.bfloat16)
+    x[70] = 0
+    ds = F.DelayedScaler(L, algo, 400.0)
+    xd = x.to(DEV)
+    outs = [ds.quantize(xd[s]) for s in range(S)]
+    torch.cuda.synchronize()
+    q2, s2 = orc.delayed_scaling(W.bits(x), L, 0 if algo == "max" else 1, 400.0)
+    got_s = np.array([_np(su)[0] for _, su in outs], np.float32)
+    np.testing.assert_array_equal(got_s.view(np.uint32), s2.view(np.uint32))
+    for s, (q, _) in enumerate(outs):
+        bad = np.flatnonzero(_np(q) != q2[s])
+        assert len(bad) == 0, f"step {s}: {len(bad)} code mismatches, first {bad[0]}"
+    if algo == "max":
+        # after the history wrapped, the scale kept falling as the oldest
+        # entries left the window, so the wrap itself is exercised
+        assert len(set(s2[L + 1:141].tolist())) >= 6
+
+
 def test_delayed_scaling_full_activation(F, orc):
     S, n = 3, 4096 * 7168
     x = _delayed_steps(S, n, 99, DEV)
