@@ -23,7 +23,8 @@
 //    the block's partial product P in fp32, then the VALU folds it in with
 //    one FMA per output: acc += P * (sa * sw).  MX scales are powers of two
 //    and are folded into the conversion instead, so the MX loop accumulates
-//    straight in the MFMAs.
+//    straight in the MFMAs (tiles whose scale bytes would push a widened
+//    code out of bf16's normal range take an exact per-32-block path).
 //  * The MFMA operands are swapped (A-operand = weight rows, B-operand =
 //    activation rows) so that each lane's four results share one token row:
 //    the combined scale is one value per lane, and the four outputs are
@@ -455,14 +456,15 @@ __device__ __forceinline__ void k_step(uint8_t* cur, uint8_t* refill, const Src<
 }
 
 // PK: the weight stages hold packed chunks (see packed_woff).
+// first_issued: the caller has already issued step 0 into l0.
 template <class C, bool PK = false>
 __device__ __forceinline__ void k_loop(uint8_t* l0, uint8_t* l1, uint8_t* l2, const Src<C>& src, int nkb,
-                                       v4f (&acc)[C::MI][C::NJ]) {
+                                       v4f (&acc)[C::MI][C::NJ], bool first_issued = false) {
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  issue<C>(l0, src, 0);
+  if (!first_issued) issue<C>(l0, src, 0);
   if (C::S == 2) {
     for (int kb = 0; kb < nkb; kb += 2) {
       k_step<C, PK>(l0, l1, src, kb, nkb, acc);
@@ -565,6 +567,140 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void block_gemm_kernel(
 }
 
 // ---- MXFP8 GEMM ---------------------------------------------------------------
+// Folding 2^(e - 127) into the FP8 -> bf16 widening (compute_mx) keeps every
+// widened code a normal bf16 only for scale bytes 10 .. 246.  Each tile
+// therefore first checks every E8M0 byte of its A and B rows over the whole
+// K range (2 * 256 * K/32 bytes for a 256 x 256 tile, L2 resident); a tile
+// with any byte outside that range runs mx_exact_tile instead, which takes
+// each 32-block's partial sum in fp32 and applies 2^(ea + eb - 254) with
+// one ldexp per output, exact for every byte.
+
+// Bit 7 of a byte lane is set in the result where that byte of v is below
+// 10 or above 246 (the "has a byte less than n" word test, applied to v
+// with n = 10 and to ~v with n = 9); zero if every byte is in 10 .. 246.
+__device__ __forceinline__ uint32_t e8m0_outside_fold_range(uint32_t v) {
+  return (((v - 0x0A0A0A0Au) & ~v) | ((0xF6F6F6F6u - v) & v)) & 0x80808080u;
+}
+
+// True if every E8M0 byte of the tile's scale rows lies in 10 .. 246: the
+// A rows [m0, m0 + ra) and B rows [n0, n0 + rb) are two contiguous byte
+// ranges (ra * srow and rb * srow bytes, multiples of 4) that the whole
+// workgroup scans with 16-byte loads (dword loads where a range is not
+// 16-byte aligned), several in flight per lane.  Every thread of the
+// workgroup must call it.
+__device__ __forceinline__ uint32_t e8m0_scan(const uint8_t* __restrict__ p, int64_t nbytes, int nt) {
+  uint32_t bad = 0u;
+  const int tid = threadIdx.x;
+  if ((reinterpret_cast<uintptr_t>(p) & 15) == 0 && (nbytes & 15) == 0) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    const int n = (int)(nbytes >> 4);
+#pragma unroll 8
+    for (int i = tid; i < n; i += nt) {
+      const uint4 v = q[i];
+      bad |= e8m0_outside_fold_range(v.x) | e8m0_outside_fold_range(v.y) | e8m0_outside_fold_range(v.z) |
+             e8m0_outside_fold_range(v.w);
+    }
+  } else {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    const int n = (int)(nbytes >> 2);
+#pragma unroll 8
+    for (int i = tid; i < n; i += nt) bad |= e8m0_outside_fold_range(q[i]);
+  }
+  return bad;
+}
+
+template <class C>
+__device__ __forceinline__ bool mx_tile_foldable(const uint8_t* __restrict__ ea, int ra,
+                                                 const uint8_t* __restrict__ eb, int rb, int srow) {
+  const uint32_t bad = e8m0_scan(ea, (int64_t)ra * srow, C::NT) | e8m0_scan(eb, (int64_t)rb * srow, C::NT);
+  return __syncthreads_or(bad != 0u) == 0;
+}
+
+// The exact MX path for one output tile (the wave's TM x TN part), reading
+// its operands straight from global memory (no LDS, no barrier): MFMA
+// window b of K step kb takes codes 128kb + 32b + 8g .. +7 of each lane's
+// row (lane group g = lane / 16), so one 16x16x32 MFMA is exactly one
+// 32-block and its fp32 result P is that block's partial sum; then
+// acc += ldexp(P, ea + eb - 254) per output.  The wave's NJ weight subtiles
+// are taken JG at a time (NJ / JG passes over K) to bound the registers.
+template <class C>
+__device__ __forceinline__ void mx_exact_tile(const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ EA,
+                                           const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ EB,
+                                           int M, int K, int m0, int n0, float* __restrict__ Y, int64_t ldy) {
+  constexpr int JG = 2;
+  static_assert(C::NJ % JG == 0, "weight subtiles per pass");
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int wm = wave % C::WM, wn = wave / C::WM, l16 = lane & 15, g = lane >> 4;
+  const int srow = K / 32, nkb = K / kBK;
+  const uint8_t* arow[C::MI];
+  const uint8_t* earow[C::MI];
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i) {
+    const int m = min(m0 + wm * C::TM + 16 * i + l16, M - 1);  // rows past M: never stored
+    arow[i] = A + (int64_t)m * lda + 8 * g;
+    earow[i] = EA + (int64_t)m * srow;
+  }
+  for (int j0 = 0; j0 < C::NJ; j0 += JG) {
+    const uint8_t* brow[JG];
+    const uint8_t* ebrow[JG];
+#pragma unroll
+    for (int jj = 0; jj < JG; ++jj) {
+      const int nb = n0 + wn * C::TN + 16 * (j0 + jj);
+      brow[jj] = B + (int64_t)(nb + l16) * ldb + 8 * g;
+      ebrow[jj] = EB + (int64_t)(nb + 4 * g) * srow;  // output rows nb + 4g .. +3
+    }
+    v4f acc[C::MI][JG];
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < JG; ++jj) acc[i][jj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kb = 0; kb < nkb; ++kb) {
+      bf16x8 xf[C::MI][4];
+      uint32_t eav[C::MI];
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const uint2 raw = *reinterpret_cast<const uint2*>(arow[i] + (int64_t)kb * kBK + 32 * b);
+          xf[i][b] = cvt8(raw.x, raw.y, 1.0f);
+        }
+        eav[i] = *reinterpret_cast<const uint32_t*>(earow[i] + 4 * kb);
+      }
+#pragma unroll
+      for (int jj = 0; jj < JG; ++jj) {
+        bf16x8 wf[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const uint2 raw = *reinterpret_cast<const uint2*>(brow[jj] + (int64_t)kb * kBK + 32 * b);
+          wf[b] = cvt8(raw.x, raw.y, 1.0f);
+        }
+        uint32_t ebv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ebv[r] = *reinterpret_cast<const uint32_t*>(ebrow[jj] + (int64_t)r * srow + 4 * kb);
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const v4f p = mfma_bf16(wf[b], xf[i][b], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+            const int ex = (int)((eav[i] >> (8 * b)) & 0xffu) - 254;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[i][jj][r] += __builtin_amdgcn_ldexpf(p[r], ex + (int)((ebv[r] >> (8 * b)) & 0xffu));
+          }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) {
+      const int m = m0 + wm * C::TM + 16 * i + l16;
+      if (m < M) {
+#pragma unroll
+        for (int jj = 0; jj < JG; ++jj)
+          store4<false>(Y, (int64_t)m * ldy + n0 + wn * C::TN + 16 * (j0 + jj) + 4 * g, acc[i][jj]);
+      }
+    }
+  }
+}
+
 template <class C>
 __global__ __launch_bounds__(C::NT, 512 / C::NT) void mx_gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ EA,
@@ -599,8 +735,16 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void mx_gemm_kernel(
     src.scale_dst = C::OFF_SB + 256 * t;
   }
 
+  // the first stage's loads go out before the range check, so its latency
+  // hides behind them
+  issue<C>(lds0, src, 0);
+  if (!mx_tile_foldable<C>(EA + (int64_t)m0 * srow, min(C::BM, M - m0), EB + (int64_t)n0 * srow, C::BN, srow)) {
+    wait_vmem<0>();
+    mx_exact_tile<C>(A, lda, EA, B, ldb, EB, M, K, m0, n0, Y, ldy);
+    return;
+  }
   v4f acc[C::MI][C::NJ];
-  k_loop<C>(lds0, lds1, lds2, src, nkb, acc);
+  k_loop<C>(lds0, lds1, lds2, src, nkb, acc, true);
   epilogue<C, false>(Y, acc, n0, [&](int r) -> int64_t { return m0 + r < M ? (int64_t)(m0 + r) * ldy : -1; });
 }
 

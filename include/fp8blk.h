@@ -196,14 +196,16 @@ int fp8_block_gemm_packed(const uint8_t *a, int64_t ld_a,
  *   M >= 0; N, K > 0 and multiples of 128; ld_a, ld_b < 2^24.
  *   y       float [M][ld_y], 16-byte aligned, ld_y % 4 == 0, ld_y >= N.
  *
- * Each scale is folded into the exact FP8 -> bf16 widening of its block's
- * codes, which keeps every widened code a normal bf16 for scale bytes 10 to
- * 246; there y meets the fp32 tolerance of the other GEMMs.  fp8_act_quant
- * gives bytes outside that range only to blocks whose amax is at most
- * 448 * 2^-118 (about 2^-109.2) or above 448 * 2^119 (about 2^127.8): such
- * a block's codes are rounded to bf16 subnormals (bytes below 10) or may
- * overflow (bytes above 246).  Scale byte 0xFF (NaN) gives unspecified
- * outputs.
+ * y meets the fp32 tolerance of the other GEMMs for every scale byte
+ * 0 .. 254 while each scaled product 2^(ea + eb - 254) * value(a) *
+ * value(b) and the sums lie in fp32's normal range (outside it, fp32's
+ * subnormal rounding or overflow applies).  Output tiles whose scale bytes
+ * all lie in 10 .. 246 fold each scale into the exact FP8 -> bf16 widening
+ * of its block's codes; a tile with any byte outside that range (from
+ * fp8_act_quant only for blocks with amax <= 448 * 2^-118 or above
+ * 448 * 2^119) takes each 32-block's partial sum in fp32 and scales it by
+ * an exact power of two instead (slower, same result contract).  Scale
+ * byte 0xFF (NaN) gives unspecified outputs.
  */
 int mxfp8_gemm(const uint8_t *a, int64_t ld_a, const uint8_t *a_e8m0,
                const uint8_t *b, int64_t ld_b, const uint8_t *b_e8m0,

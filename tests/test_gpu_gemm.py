@@ -409,6 +409,54 @@ def test_mx_gemm_exact_at_the_scale_byte_range_edges(F, orc, edge):
         assert_parity(_np(y), yr, bnd, False, f"mx scale bytes at the {edge} edge")
 
 
+def _mx_codes(rng, rows, K):
+    c = rng.integers(0, 0x7F, size=(rows, K)).astype(np.uint8)      # 0x7F is NaN
+    return c | (rng.integers(0, 2, size=(rows, K)).astype(np.uint8) << 7)
+
+
+@pytest.mark.parametrize("edge", ["low", "high"])
+@pytest.mark.parametrize("M,N", [(128, 128), (2048, 256)])
+def test_mx_gemm_exact_outside_the_fold_range(F, orc, edge, M, N):
+    """Scale bytes 0..9 or 247..254 on one operand (every tile takes the
+    exact per-32-block path), the other operand's bytes chosen so every
+    product and sum stays in fp32's normal range; each operand in each role,
+    on the 128 x 128 and the 256 x 256 tile shapes."""
+    rng = np.random.default_rng(31 + (edge == "high") + M)
+    K = 256
+    a, b = _mx_codes(rng, M, K), _mx_codes(rng, N, K)
+    if edge == "low":     # products >= 2^(0 + 146 - 272) = 2^-126
+        ea = rng.integers(0, 10, size=(M, K // 32)).astype(np.uint8)
+        eb = rng.integers(146, 234, size=(N, K // 32)).astype(np.uint8)
+    else:                 # products <= 2^(254 + 100 - 254 + 17.6); sums < 2^126
+        ea = rng.integers(247, 255, size=(M, K // 32)).astype(np.uint8)
+        eb = rng.integers(26, 101, size=(N, K // 32)).astype(np.uint8)
+    cases = [(a, ea, b, eb)] + ([(b, eb, a, ea)] if M == N else [])
+    for x, ex, w, ew in cases:
+        y = F.mxfp8_gemm(*[torch.from_numpy(v).to(DEV) for v in (x, ex, w, ew)])
+        torch.cuda.synchronize()
+        yr, bnd = orc.mx_gemm(x, ex, w, ew)
+        assert np.all(np.isfinite(yr)) and np.all(bnd > 0)
+        assert_parity(_np(y), yr, bnd, False, f"mx scale bytes beyond the {edge} fold edge, {x.shape[0]}x{w.shape[0]}")
+
+
+def test_mx_gemm_exact_and_folded_tiles_in_one_launch(F, orc):
+    """Out-of-range bytes in a few rows and columns only: the tiles holding
+    them take the exact path (mixing in-range and out-of-range rows), the
+    others the folded path, in the same launch (256 x 256 tiles)."""
+    rng = np.random.default_rng(40)
+    M, N, K = 2048, 512, 384
+    a, b = _mx_codes(rng, M, K), _mx_codes(rng, N, K)
+    ea = rng.integers(120, 135, size=(M, K // 32)).astype(np.uint8)
+    eb = rng.integers(146, 160, size=(N, K // 32)).astype(np.uint8)
+    ea[300:304, 5] = rng.integers(0, 10, size=4)          # tile row 1
+    ea[1800, :] = 3                                       # tile row 7
+    eb[260, 11] = 8                                       # tile column 1, with in-range A rows
+    y = F.mxfp8_gemm(*[torch.from_numpy(v).to(DEV) for v in (a, ea, b, eb)])
+    torch.cuda.synchronize()
+    yr, bnd = orc.mx_gemm(a, ea, b, eb)
+    assert_parity(_np(y), yr, bnd, False, "mx with exact and folded tiles")
+
+
 # ---- MoE combine ---------------------------------------------------------------
 def _combine_check(F, orc, y, tr, gates, out_dtype, what):
     out = F.fp8_moe_combine(y, tr, gates, out_dtype)
