@@ -37,6 +37,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -55,6 +56,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=50,
                    help="untimed steps first; under sustained MFMA load the clock dips for the "
                         "first ~25 ms and settles after ~50 steps")
+    p.add_argument("--settle-ms", type=float, default=150.0,
+                   help="after the warm-up steps, keep stepping until this much time has passed "
+                        "before the timed steps (the clock settles within ~50 ms of MFMA load)")
     p.add_argument("--no-legs", action="store_true", help="time the headline step only")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ceilings", action="store_true",
@@ -219,15 +223,32 @@ def main():
     # graph of the step measured the same).  In every timed step the block
     # GEMM is bracketed by events on the library's stream, so its average
     # duration comes from the timed region itself.
-    for _ in range(args.warmup):
+    def step():
         aq()
         gemm()
+
+    for _ in range(args.warmup):
+        step()
+    # Then settle on time, not on a step count: under sustained MFMA load the
+    # clock dips for the first ~25 ms and settles after ~50 ms, so steps
+    # keep running until args.settle_ms of device time has passed (whatever
+    # --warmup was), and the timed steps start from the settled clock.
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    settle_steps = 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            step()
+        settle_steps += 10
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1 in ev:
+    for es, e0, e1 in ev:
+        es.record(stream)
         aq()
         e0.record(stream)
         gemm()
@@ -237,7 +258,10 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     flops = 2.0 * M * N * K
     value = flops / (wall / args.steps) / 1e12
-    t_gemm = sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev) * 1e-3
+    gemm_ms = [e0.elapsed_time(e1) for _, e0, e1 in ev]
+    step_ms = [es.elapsed_time(e1) for es, _, e1 in ev]
+    t_gemm = sum(gemm_ms) / len(gemm_ms) * 1e-3
+    t_gemm_median = statistics.median(gemm_ms) * 1e-3
 
     # act_quant alone: 17 us, so timed back to back from a captured graph
     t_aq = timed_graph(torch, aq, max(args.steps, 10))
@@ -248,6 +272,8 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
                 "kernel": "block_gemm_kernel", "avg_launch_us": round(t_gemm * 1e6, 2),
+                "median_launch_us": round(t_gemm_median * 1e6, 2),
+                "achieved_at_median": round(flops / t_gemm_median / 1e12, 1),
                 "algorithmic_bytes": gemm_bytes,
                 "frac_of_bf16_dense_peak": round(achieved / PEAK_BF16_TFLOPS, 4)}
     legs["prefill"] = {"act_quant_us": round(t_aq * 1e6, 2),
@@ -262,6 +288,8 @@ def main():
     if not args.no_cpu_baseline:
         import numpy as np
         import oracle as O
+        sys.path.insert(0, os.path.join(HERE, "tests"))
+        import parity as P
         xb = W.bits(x)
         ow, osw = O.weight_quant(W.bits(W.prefill_linear(device=dev).w), 0)   # offline, untimed
         rows = args.cpu_rows or 32
@@ -279,6 +307,14 @@ def main():
                "cores": O.num_threads(), "kind": "oracle",
                "sample": f"act_quant + block GEMM of the first {rows} of {M} token rows "
                          f"(all {N} outputs, K {K}), {t_cpu:.1f} s"}
+        # the same oracle rows against the timed step's output (outside the
+        # timed region): worst |err| / allowed over every sampled output
+        yr, bnd = O.block_gemm(oa, osa, ow, osw)
+        yg = y[:rows].float().cpu().numpy().astype(np.float64)
+        ok, worst = P.check_bf16(yg, yr, bnd)
+        cpu["parity_prefill"] = {"worst_err_over_allowed": round(worst, 5), "outputs": int(yg.size),
+                                 "all_within": bool(ok.all())}
+        del yr, bnd, yg
         # the same oracle on one thread, over a sample sized to a few seconds
         all_threads = O.num_threads()
         rows1 = max(1, min(rows, int(rows * 4.0 / max(t_cpu * all_threads, 1e-3))))
@@ -337,6 +373,9 @@ def main():
     if not args.no_legs:
         legs.update(run_legs(torch, F, W, dev, args.only))
 
+    if cpu is not None and not args.no_legs and not args.only:
+        cpu["configs"] = oracle_configs(torch, F, W, O, P, dev)
+
     out = {
         "metric": "block-scaled FP8 GEMM TFLOPS (incl. act_quant) and % of MI355X FP8 MFMA peak",
         "value": round(value, 2),
@@ -345,6 +384,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms_median": round(statistics.median(step_ms), 4),
+        "settle": {"ms": round(settle_ms, 1), "steps": settle_steps,
+                   "note": "untimed steps after the warm-up, until the clock settled"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -363,6 +405,113 @@ def main():
         "legs": legs,
     }
     print(json.dumps(out), flush=True)
+
+
+def oracle_configs(torch, F, W, O, P, dev):
+    """The oracle on a bounded sample of every workload, timed on the host
+    cores, and compared with the GPU's output for the same sample (run once
+    more, outside every timed region): worst |err| / allowed per config
+    (1.0 is the edge of the tolerance; codes are compared bit for bit
+    separately in the tests).  The prefill case is covered by the headline's
+    own sample above."""
+    import numpy as np
+    res = {}
+    cores = O.num_threads()
+
+    def rec(name, yg, yr, bnd, bf16, macs, t, sample):
+        ok, worst = (P.check_bf16 if bf16 else P.check_f32)(yg, yr, bnd)
+        res[name] = {"worst_err_over_allowed": round(worst, 5), "all_within": bool(ok.all()),
+                     "outputs": int(np.asarray(yg).size),
+                     "oracle_s": round(t, 3), "oracle_TFLOPs": round(2.0 * macs / max(t, 1e-9) / 1e12, 6),
+                     "cores": cores, "sample": sample}
+
+    # tiny linear, 16 x 512 -> 256, fp32 out: the whole output
+    c = W.tiny_linear()
+    a, sa = F.fp8_act_quant(c.x.to(dev), 128, "fp32")
+    wq, ws = F.fp8_weight_quant(c.w.to(dev), "fp32")
+    yg = F.fp8_block_gemm(a, sa, wq, ws, torch.float32).cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    oa, osa = O.act_quant(W.bits(c.x), 128, 0)
+    ow, osw = O.weight_quant(W.bits(c.w), 0)
+    yr, bnd = O.block_gemm(oa, osa, ow, osw)
+    rec("tiny", yg, yr, bnd, False, 16 * 512 * 256, time.perf_counter() - t0, "all 16 x 256 outputs")
+
+    # decode, 8192 -> 28672, ue8m0, bf16 out: every token row, weight rows
+    # 0..255 and the last 256 (whole 128-row scale blocks)
+    c = W.decode_linear(device=dev)
+    N, K = c.w.shape
+    wq, ws = F.fp8_weight_quant(c.w, "ue8m0")
+    wp = F.fp8_weight_pack(wq)
+    cols = np.r_[0:256, N - 256:N]
+    t0 = time.perf_counter()
+    ow, osw = O.weight_quant(W.bits(c.w[torch.as_tensor(cols, device=dev)]), 1)
+    t_w = time.perf_counter() - t0
+    for M in (1, 8, 32, 128):
+        x = c.x[:M].contiguous()
+        a, sa = F.fp8_act_quant(x, 128, "ue8m0")
+        yg = F.fp8_block_gemm_packed(a, sa, wp, ws, torch.bfloat16)[:, torch.as_tensor(cols, device=dev)]
+        yg = yg.float().cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        oa, osa = O.act_quant(W.bits(x), 128, 1)
+        yr, bnd = O.block_gemm(oa, osa, ow, osw)
+        rec(f"decode_M{M}", yg, yr, bnd, True, M * len(cols) * K, time.perf_counter() - t0 + t_w,
+            f"all {M} token rows x weight rows 0-255 and {N - 256}-{N - 1} (packed weights)")
+    del c, wq, ws, wp
+    torch.cuda.empty_cache()
+
+    # MXFP8 8192^3, fp32 out: 8 rows spread over A, every column
+    A, B = W.mx_case(device=dev)
+    M = A.shape[0]
+    qa, ea = F.fp8_act_quant(A, 32, "e8m0")
+    qb, eb = F.fp8_act_quant(B, 32, "e8m0")
+    rows = np.linspace(0, M - 1, 8).astype(np.int64)
+    yg = F.mxfp8_gemm(qa, ea, qb, eb)[torch.as_tensor(rows, device=dev)].cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    oa, oea = O.act_quant(W.bits(A[torch.as_tensor(rows, device=dev)]), 32, 2)
+    ob, oeb = O.act_quant(W.bits(B), 32, 2)
+    yr, bnd = O.mx_gemm(oa, oea, ob, oeb)
+    rec("mx_8192", yg, yr, bnd, False, len(rows) * B.shape[0] * A.shape[1], time.perf_counter() - t0,
+        f"token rows {rows.tolist()} x all {B.shape[0]} columns (quant of B included)")
+    del A, B, qa, ea, qb, eb
+    torch.cuda.empty_cache()
+
+    # grouped MoE, 256 experts: routed rows of the largest expert (first,
+    # last, one past a tile) and of three single-row experts
+    case = W.moe_case(device=dev)
+    E, N, K = case.w.shape
+    a, sa = F.fp8_act_quant(case.x, 128, "fp32")
+    wq = torch.empty(E, N, K, dtype=torch.uint8, device=dev)
+    ws = torch.empty(E, N // 128, K // 128, dtype=torch.float32, device=dev)
+    for e in range(E):
+        F.fp8_weight_quant(case.w[e], "fp32", q=wq[e], scales=ws[e])
+    wp = F.fp8_weight_pack(wq)
+    del wq
+    ri, offs = case.row_index.to(dev), case.offs.to(dev)
+    yfull = F.fp8_grouped_gemm_packed(a, sa, ri, offs, wp, ws, torch.bfloat16)
+    offs_np = case.offs.numpy()
+    counts = offs_np[1:] - offs_np[:-1]
+    big = int(np.argmax(counts))
+    small = [e for e in range(E) if counts[e] == 1][:3]
+    rows = sorted({int(offs_np[big]), int(offs_np[big + 1]) - 1, int(offs_np[big]) + 130}
+                  | {int(offs_np[e]) for e in small})
+    yg = yfull[torch.as_tensor(rows, device=dev)].float().cpu().numpy().astype(np.float64)
+    del yfull, wp, ws, a, sa
+    t0 = time.perf_counter()
+    experts = sorted({int(np.searchsorted(offs_np, r, side="right") - 1) for r in rows})
+    toks = sorted({int(case.row_index[r]) for r in rows})
+    oa_full = np.zeros((case.x.shape[0], K), np.uint8)
+    osa_full = np.ones((case.x.shape[0], K // 128), np.float32)
+    oa, osa = O.act_quant(W.bits(case.x[torch.as_tensor(toks, device=dev)]), 128, 0)
+    oa_full[toks], osa_full[toks] = oa, osa
+    wl, sl = [None] * E, [None] * E
+    for e in experts:
+        wl[e], sl[e] = O.weight_quant(W.bits(case.w[e]), 0)
+    yr, bnd = O.grouped_gemm(oa_full, osa_full, case.row_index.numpy(), offs_np, wl, sl, rows=rows)
+    rec("moe_256x8", yg, yr, bnd, True, len(rows) * N * K, time.perf_counter() - t0,
+        f"routed rows {rows} (experts {experts}, weights quantised by the oracle)")
+    del case
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_legs(torch, F, W, dev, only=""):
