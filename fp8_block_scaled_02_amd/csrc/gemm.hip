@@ -87,8 +87,17 @@ struct Cfg {
   static_assert(S * BUF <= 160 * 1024, "LDS capacity");
 };
 
-// LDS byte offset of logical 16-byte chunk `ch` (0..7) of tile row `r`.
-__device__ __forceinline__ int lds_off(int r, int ch) { return r * 128 + ((ch ^ (r & 7)) << 4); }
+// LDS byte offset of logical 16-byte chunk `ch` (0..7) of tile row `r`: the
+// chunks of a row are XOR-swizzled by the row's low 3 bits, which keeps the
+// 16 x 16 fragment reads (16 rows x 2 chunks per 32 lanes) conflict-free.
+// S16 also folds row bit 4 into chunk bit 2: the 32 x 32 fragment reads
+// (32 consecutive rows in one 32-lane half) otherwise pair rows r and r + 16
+// on the same banks (measured on MI355X: about 4 conflict cycles per
+// ds_read_b128 without it, none with it).
+template <bool S16 = false>
+__device__ __forceinline__ int row_swz(int r) { return (r & 7) ^ (S16 ? (r >> 2) & 4 : 0); }
+template <bool S16 = false>
+__device__ __forceinline__ int lds_off(int r, int ch) { return r * 128 + ((ch ^ row_swz<S16>(r)) << 4); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -156,22 +165,24 @@ struct Src {
 // (l & 7) ^ (row & 7) = (l & 7) ^ (l >> 3).  arow_off(r) is the byte offset
 // of activation row r from abase; woff(qw, lane) that of lane's 16 bytes of
 // W group qw from wbase (row_major_woff or packed_woff).
-template <class C, class ARow, class WOff>
+// (With S16 the swizzle of row 8q + (l >> 3) also carries bit 1 of q.)
+template <class C, bool S16 = false, class ARow, class WOff>
 __device__ __forceinline__ void make_code_src(Src<C>& s, ARow arow_off, WOff woff) {
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const uint32_t chunk = (uint32_t)((lane & 7) ^ (lane >> 3));
 #pragma unroll
   for (int i = 0; i < C::NI; ++i) {
     const int q = wave + C::NW * i;
+    const uint32_t chunk = (uint32_t)((lane & 7) ^ row_swz<S16>(8 * q + (lane >> 3)));
     s.code[i] = q < C::BM / 8 ? arow_off(8 * q + (lane >> 3)) + chunk * 16u : woff(q - C::BM / 8, lane);
   }
 }
 
 // Row-major weights [rows][ld]: W group qw is tile rows 8qw .. 8qw+7, in the
 // swizzled row layout of the A groups.
+template <bool S16 = false>
 __device__ __forceinline__ uint32_t row_major_woff(int qw, int lane, int64_t ld) {
   const int r = 8 * qw + (lane >> 3);
-  return (uint32_t)(r * ld) + (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+  return (uint32_t)(r * ld) + (uint32_t)(((lane & 7) ^ row_swz<S16>(r)) * 16);
 }
 
 // ---- packed weight layout ---------------------------------------------------
@@ -480,12 +491,16 @@ __device__ __forceinline__ void k_loop(uint8_t* l0, uint8_t* l1, uint8_t* l2, co
   }
 }
 
+// Four consecutive outputs: bf16 by v_cvt_pk_bf16_f32 (round to nearest
+// even, two values per instruction), or fp32.
 template <bool BF16>
 __device__ __forceinline__ void store4(void* __restrict__ y, int64_t off, const v4f v) {
   if (BF16) {
+    const bf16x2 b0 = {(__bf16)v[0], (__bf16)v[1]};
+    const bf16x2 b1 = {(__bf16)v[2], (__bf16)v[3]};
     uint2 p;
-    p.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-    p.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+    p.x = __builtin_bit_cast(uint32_t, b0);
+    p.y = __builtin_bit_cast(uint32_t, b1);
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + off) = p;
   } else {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + off) = make_float4(v[0], v[1], v[2], v[3]);
@@ -510,6 +525,179 @@ __device__ __forceinline__ void epilogue(void* __restrict__ y, const v4f (&acc)[
   }
 }
 
+// ---- the block GEMM's K step on 32 x 32 x 16 MFMAs ---------------------------
+// The same tiles, LDS stages and loads as compute_block, with the products on
+// v_mfma_f32_32x32x16_bf16: a 32-cycle MFMA that lets the VALU widening and
+// rescale issue beside it far more freely than the 16-cycle 16 x 16 x 32 form
+// (measured on MI355X with operands in registers: 6 VALU instructions per
+// 32 x 32 MFMA cost x1.12, while 3 per 16 x 16 MFMA cost x1.38).
+//
+// A wave's 64 x 64 tile is 2 x 2 blocks of 32 x 32 (weight rows x tokens).
+// Lane l = 32h + r (h = 0, 1) holds row r of a 32-row fragment and takes
+// K bytes 64h .. 64h+63 of the 128-wide K block: MFMA kk (0..7) multiplies
+// bytes 64h + 8kk .. +7 of both operands, so every K of the block is
+// multiplied exactly once.  Each lane reads 16 bytes (two MFMAs' worth) of a
+// fragment per ds_read_b128: 8 lanes of consecutive rows cover 8 distinct
+// 16-byte columns of the XOR-swizzled rows (or 128 contiguous bytes of a
+// packed chunk), so the reads are conflict-free.
+//
+// The four 32 x 32 blocks accumulate the K block's partial P in four
+// independent MFMA chains; P is folded into acc (acc += P * sa * sw, one FMA
+// per output) during the next K block, each block's fold right before the
+// first MFMA that overwrites its P.  Output: lane l of block (i, j) holds
+// tile token row 32i + r and weight rows 32j + 8q + 4h .. +3 in values
+// 4q .. 4q+3.
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ v16f mfma32_bf16(bf16x8 a, bf16x8 b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Offset in the stage's weight region of the 16 bytes that lane (row, h)
+// reads for kk2 = 0 (w32_at gives the others): packed chunks (h, row / 16),
+// or swizzled rows (chunk 4h + kk2 of a row sits at lds_off(row, 4h) ^
+// (kk2 << 4)).
+template <class C, bool PK>
+__device__ __forceinline__ int w32_off(int row, int h) {
+  return PK ? ((h * (C::BN / 16) + (row >> 4)) << 10) + 16 * (row & 15) : lds_off<true>(row, 4 * h);
+}
+template <bool PK>
+__device__ __forceinline__ int w32_at(int off, int kk2) {
+  return PK ? off + 256 * kk2 : off ^ (kk2 << 4);
+}
+
+// One K block: accumulate this block's partials into P (its scales into sn)
+// while folding the previous block's partials Pp (scales sp) into acc: in
+// MFMA window kk every chain folds its values 2kk, 2kk+1, so the 64 FMAs
+// of a block issue beside its 32 MFMAs instead of in one burst (empty asm
+// statements tie each window's folds to the next window's operands).
+template <class C, bool PK, class Hook>
+__device__ __forceinline__ void compute_block32(const uint8_t* buf, v16f (&acc)[2][2], v16f (&P)[2][2],
+                                                const v16f (&Pp)[2][2], const float (&sp)[2], float (&sn)[2],
+                                                Hook hook) {
+  static_assert(C::TM == 64 && C::TN == 64, "2 x 2 blocks of 32 x 32 per wave");
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int wm = wave % C::WM, wn = wave / C::WM, r = lane & 31, h = lane >> 5;
+  const float* sa = reinterpret_cast<const float*>(buf + C::OFF_SA);
+  const float* sw = reinterpret_cast<const float*>(buf + C::OFF_SB);
+  const uint8_t* wt = buf + C::OFF_W;
+  uint4 ra[2][2], rw[2][2];  // [slot][fragment]: 16 code bytes = MFMAs 2kk2, 2kk2+1
+  // chunk 4h + kk2 of a swizzled row sits at lds_off(row, 4h) ^ (kk2 << 4)
+  // (kk2 < 4 only flips bits 4-5 of the chunk offset)
+  const int a_off = lds_off<true>(wm * 64 + r, 4 * h);  // fragment 1 is 32 rows (4096 bytes) further
+  const int w_off = w32_off<C, PK>(wn * 64 + r, h);
+  // fragment 1 is 32 rows further: two packed chunks (2048 bytes) or 4096 bytes of rows
+  constexpr int w_frag = PK ? 2048 : 4096;
+  auto load = [&](int sl, int kk2) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      ra[sl][i] = *reinterpret_cast<const uint4*>(buf + 4096 * i + (a_off ^ (kk2 << 4)));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      rw[sl][j] = *reinterpret_cast<const uint4*>(wt + w_frag * j + w32_at<PK>(w_off, kk2));
+  };
+  load(0, 0);
+  const float swv = sw[(wn * 64) / 128];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) sn[i] = sa[wm * 64 + 32 * i + r] * swv;
+  hook();
+#pragma unroll
+  for (int kk2 = 0; kk2 < 4; ++kk2) {
+    const int sl = kk2 & 1;
+    if (kk2 < 3) load(sl ^ 1, kk2 + 1);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int kk = 2 * kk2 + half;
+      bf16x8 xa[2], xw[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        xa[i] = half ? cvt8(ra[sl][i].z, ra[sl][i].w, 1.0f) : cvt8(ra[sl][i].x, ra[sl][i].y, 1.0f);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        xw[j] = half ? cvt8(rw[sl][j].z, rw[sl][j].w, 1.0f) : cvt8(rw[sl][j].x, rw[sl][j].y, 1.0f);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          P[i][j] = mfma32_bf16(xw[j], xa[i], kk == 0 ? v16f{} : P[i][j]);
+#pragma unroll
+          for (int v = 2 * kk; v < 2 * kk + 2; ++v) acc[i][j][v] = __builtin_fmaf(Pp[i][j][v], sp[i], acc[i][j][v]);
+        }
+      if (kk < 7) {
+        // this window's folds complete before the next window's operands
+        // exist (keeps them spread over the block)
+        asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]));
+      }
+    }
+  }
+}
+
+template <class C, bool PK>
+__device__ __forceinline__ void k_loop32(uint8_t* l0, uint8_t* l1, const Src<C>& src, int nkb, v16f (&acc)[2][2]) {
+  static_assert(C::S == 2, "two LDS stages");
+  // partials of the even and odd K blocks; the fold of the block before the
+  // first is a no-op on zeros
+  v16f P0[2][2], P1[2][2];
+  float s0[2] = {0.0f, 0.0f}, s1[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      acc[i][j] = v16f{};
+      P1[i][j] = v16f{};
+    }
+  issue<C>(l0, src, 0);
+  auto sync = [&]() {
+    wait_vmem<0>();
+    __syncthreads();
+  };
+  // pairs of blocks with fixed roles for P0 / P1 (no copies between them)
+  int kb = 0;
+  for (; kb + 1 < nkb; kb += 2) {
+    sync();
+    compute_block32<C, PK>(l0, acc, P0, P1, s1, s0, [&]() { issue<C>(l1, src, kb + 1); });
+    sync();
+    compute_block32<C, PK>(l1, acc, P1, P0, s0, s1, [&]() {
+      if (kb + 2 < nkb) issue<C>(l0, src, kb + 2);
+    });
+  }
+  if (kb < nkb) {  // an odd last block: its partials end in P0
+    sync();
+    compute_block32<C, PK>(l0, acc, P0, P1, s1, s0, []() {});
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(P0[i][j][v], s0[i], acc[i][j][v]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(P1[i][j][v], s1[i], acc[i][j][v]);
+  }
+}
+
+template <class C, bool BF16, class RowOff>
+__device__ __forceinline__ void epilogue32(void* __restrict__ y, const v16f (&acc)[2][2], int n0, RowOff row_off) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int wm = wave % C::WM, wn = wave / C::WM, r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t base = row_off(wm * 64 + 32 * i + r);
+    if (base >= 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          store4<BF16>(y, base + n0 + wn * 64 + 32 * j + 8 * q + 4 * h,
+                       v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]});
+    }
+  }
+}
+
 // Stage arrays: a kernel declares all three (unused ones cost nothing; the
 // compiler drops them) so one body serves S = 2 and S = 3.
 #define FP8B_STAGES(C)                                                          \
@@ -520,7 +708,7 @@ __device__ __forceinline__ void epilogue(void* __restrict__ y, const v4f (&acc)[
 // ---- block-scaled GEMM ------------------------------------------------------
 // Occupancy: 512-thread tiles run one workgroup per CU (2 waves per SIMD);
 // 256-thread tiles two.
-template <class C, bool BF16, bool PK>
+template <class C, bool BF16, bool PK, bool M32 = false>
 __global__ __launch_bounds__(C::NT, 512 / C::NT) void block_gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ SA,
     const uint8_t* __restrict__ W, int64_t ldw, const float* __restrict__ SW, int M, int N, int K,
@@ -541,13 +729,13 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void block_gemm_kernel(
   if (PK) {
     src.wbase = W + (int64_t)(n0 / 16) * 1024;
     src.wstep = (size_t)N * kBK;
-    make_code_src<C>(src, [&](int r) { return (uint32_t)(min(r, mlast) * lda); },
-                     [&](int qw, int l) { return packed_woff(qw, l, N / 16, C::BN / 16); });
+    make_code_src<C, M32>(src, [&](int r) { return (uint32_t)(min(r, mlast) * lda); },
+                          [&](int qw, int l) { return packed_woff(qw, l, N / 16, C::BN / 16); });
   } else {
     src.wbase = W + (int64_t)n0 * ldw;
     src.wstep = kBK;
-    make_code_src<C>(src, [&](int r) { return (uint32_t)(min(r, mlast) * lda); },
-                     [&](int qw, int l) { return row_major_woff(qw, l, ldw); });
+    make_code_src<C, M32>(src, [&](int r) { return (uint32_t)(min(r, mlast) * lda); },
+                          [&](int qw, int l) { return row_major_woff<M32>(qw, l, ldw); });
   }
   src.scale_dst = -1;
   src.sbase = reinterpret_cast<const uint8_t*>(SA + (int64_t)m0 * nkb);
@@ -561,9 +749,15 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void block_gemm_kernel(
     src.scale_dst = C::OFF_SB;
   }
 
-  v4f acc[C::MI][C::NJ];
-  k_loop<C, PK>(lds0, lds1, lds2, src, nkb, acc);
-  epilogue<C, BF16>(Y, acc, n0, [&](int r) -> int64_t { return m0 + r < M ? (int64_t)(m0 + r) * ldy : -1; });
+  if constexpr (M32) {
+    v16f acc[2][2];
+    k_loop32<C, PK>(lds0, lds1, src, nkb, acc);
+    epilogue32<C, BF16>(Y, acc, n0, [&](int r) -> int64_t { return m0 + r < M ? (int64_t)(m0 + r) * ldy : -1; });
+  } else {
+    v4f acc[C::MI][C::NJ];
+    k_loop<C, PK>(lds0, lds1, lds2, src, nkb, acc);
+    epilogue<C, BF16>(Y, acc, n0, [&](int r) -> int64_t { return m0 + r < M ? (int64_t)(m0 + r) * ldy : -1; });
+  }
 }
 
 // ---- MXFP8 GEMM ---------------------------------------------------------------
@@ -1158,6 +1352,9 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
 #ifndef FP8B_BLOCK_STAGES
 #define FP8B_BLOCK_STAGES 2
 #endif
+#ifndef FP8B_BLOCK_MMA32
+#define FP8B_BLOCK_MMA32 1  // block GEMM K step on 32 x 32 x 16 MFMAs (0: 16 x 16 x 32)
+#endif
 #ifndef FP8B_MX_CFG
 #define FP8B_MX_CFG 256, 256, 4, 2
 #endif
@@ -1240,17 +1437,17 @@ static void launch_decode(const uint8_t* a, int64_t lda, const float* sa, const 
     launch_decode_nj<4, PK, FP8B_DEC4>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
 }
 
-template <class C, bool PK>
+template <class C, bool PK, bool M32 = false>
 static void launch_block(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
                          const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
                          hipStream_t s) {
   const int64_t tiles = ((M + C::BM - 1) / C::BM) * (N / C::BN);
   const dim3 grid((unsigned)tiles), block(C::NT);
   if (out_bf16)
-    hipLaunchKernelGGL((block_gemm_kernel<C, true, PK>), grid, block, 0, s, a, lda, sa, w, ldw, sw, (int)M,
+    hipLaunchKernelGGL((block_gemm_kernel<C, true, PK, M32>), grid, block, 0, s, a, lda, sa, w, ldw, sw, (int)M,
                        (int)N, (int)K, y, ldy);
   else
-    hipLaunchKernelGGL((block_gemm_kernel<C, false, PK>), grid, block, 0, s, a, lda, sa, w, ldw, sw, (int)M,
+    hipLaunchKernelGGL((block_gemm_kernel<C, false, PK, M32>), grid, block, 0, s, a, lda, sa, w, ldw, sw, (int)M,
                        (int)N, (int)K, y, ldy);
 }
 
@@ -1274,7 +1471,7 @@ static void launch_block_any(const uint8_t* a, int64_t lda, const float* sa, con
   } else if (M <= 128)
     launch_block<SmallMCfg, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
   else
-    launch_block<BlockCfg, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+    launch_block<BlockCfg, PK, FP8B_BLOCK_MMA32 != 0>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
 }
 
 int launch_block_gemm(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
