@@ -87,17 +87,10 @@ struct Cfg {
   static_assert(S * BUF <= 160 * 1024, "LDS capacity");
 };
 
-// LDS byte offset of logical 16-byte chunk `ch` (0..7) of tile row `r`: the
+// LDS byte offset of logical 16-byte chunk `ch` (0..7) of tile row `r` (the
 // chunks of a row are XOR-swizzled by the row's low 3 bits, which keeps the
-// 16 x 16 fragment reads (16 rows x 2 chunks per 32 lanes) conflict-free.
-// S16 also folds row bit 4 into chunk bit 2: the 32 x 32 fragment reads
-// (32 consecutive rows in one 32-lane half) otherwise pair rows r and r + 16
-// on the same banks (measured on MI355X: about 4 conflict cycles per
-// ds_read_b128 without it, none with it).
-template <bool S16 = false>
-__device__ __forceinline__ int row_swz(int r) { return (r & 7) ^ (S16 ? (r >> 2) & 4 : 0); }
-template <bool S16 = false>
-__device__ __forceinline__ int lds_off(int r, int ch) { return r * 128 + ((ch ^ row_swz<S16>(r)) << 4); }
+// 16 x 16 fragment reads conflict-free).
+__device__ __forceinline__ int lds_off(int r, int ch) { return r * 128 + ((ch ^ (r & 7)) << 4); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -165,24 +158,22 @@ struct Src {
 // (l & 7) ^ (row & 7) = (l & 7) ^ (l >> 3).  arow_off(r) is the byte offset
 // of activation row r from abase; woff(qw, lane) that of lane's 16 bytes of
 // W group qw from wbase (row_major_woff or packed_woff).
-// (With S16 the swizzle of row 8q + (l >> 3) also carries bit 1 of q.)
-template <class C, bool S16 = false, class ARow, class WOff>
+template <class C, class ARow, class WOff>
 __device__ __forceinline__ void make_code_src(Src<C>& s, ARow arow_off, WOff woff) {
   const int lane = threadIdx.x & 63, wave = wave_id();
+  const uint32_t chunk = (uint32_t)((lane & 7) ^ (lane >> 3));
 #pragma unroll
   for (int i = 0; i < C::NI; ++i) {
     const int q = wave + C::NW * i;
-    const uint32_t chunk = (uint32_t)((lane & 7) ^ row_swz<S16>(8 * q + (lane >> 3)));
     s.code[i] = q < C::BM / 8 ? arow_off(8 * q + (lane >> 3)) + chunk * 16u : woff(q - C::BM / 8, lane);
   }
 }
 
 // Row-major weights [rows][ld]: W group qw is tile rows 8qw .. 8qw+7, in the
 // swizzled row layout of the A groups.
-template <bool S16 = false>
 __device__ __forceinline__ uint32_t row_major_woff(int qw, int lane, int64_t ld) {
   const int r = 8 * qw + (lane >> 3);
-  return (uint32_t)(r * ld) + (uint32_t)(((lane & 7) ^ row_swz<S16>(r)) * 16);
+  return (uint32_t)(r * ld) + (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
 }
 
 // ---- packed weight layout ---------------------------------------------------
@@ -537,9 +528,11 @@ __device__ __forceinline__ void epilogue(void* __restrict__ y, const v4f (&acc)[
 // K bytes 64h .. 64h+63 of the 128-wide K block: MFMA kk (0..7) multiplies
 // bytes 64h + 8kk .. +7 of both operands, so every K of the block is
 // multiplied exactly once.  Each lane reads 16 bytes (two MFMAs' worth) of a
-// fragment per ds_read_b128: 8 lanes of consecutive rows cover 8 distinct
-// 16-byte columns of the XOR-swizzled rows (or 128 contiguous bytes of a
-// packed chunk), so the reads are conflict-free.
+// fragment per ds_read_b128.  Packed weight chunks read conflict-free; 32
+// consecutive XOR-swizzled activation rows in a 32-lane half cost about 4
+// LDS bank-conflict cycles per read on MI355X, one per MFMA.  Storing the
+// activation tile in the packed chunk order instead removes them, but its
+// half-line (64-byte) global loads made the prefill GEMM 10% slower.
 //
 // The four 32 x 32 blocks accumulate the K block's partial P in four
 // independent MFMA chains; P is folded into acc (acc += P * sa * sw, one FMA
@@ -559,7 +552,7 @@ __device__ __forceinline__ v16f mfma32_bf16(bf16x8 a, bf16x8 b, v16f c) {
 // (kk2 << 4)).
 template <class C, bool PK>
 __device__ __forceinline__ int w32_off(int row, int h) {
-  return PK ? ((h * (C::BN / 16) + (row >> 4)) << 10) + 16 * (row & 15) : lds_off<true>(row, 4 * h);
+  return PK ? ((h * (C::BN / 16) + (row >> 4)) << 10) + 16 * (row & 15) : lds_off(row, 4 * h);
 }
 template <bool PK>
 __device__ __forceinline__ int w32_at(int off, int kk2) {
@@ -584,7 +577,7 @@ __device__ __forceinline__ void compute_block32(const uint8_t* buf, v16f (&acc)[
   uint4 ra[2][2], rw[2][2];  // [slot][fragment]: 16 code bytes = MFMAs 2kk2, 2kk2+1
   // chunk 4h + kk2 of a swizzled row sits at lds_off(row, 4h) ^ (kk2 << 4)
   // (kk2 < 4 only flips bits 4-5 of the chunk offset)
-  const int a_off = lds_off<true>(wm * 64 + r, 4 * h);  // fragment 1 is 32 rows (4096 bytes) further
+  const int a_off = lds_off(wm * 64 + r, 4 * h);  // fragment 1 is 32 rows (4096 bytes) further
   const int w_off = w32_off<C, PK>(wn * 64 + r, h);
   // fragment 1 is 32 rows further: two packed chunks (2048 bytes) or 4096 bytes of rows
   constexpr int w_frag = PK ? 2048 : 4096;
@@ -729,13 +722,13 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void block_gemm_kernel(
   if (PK) {
     src.wbase = W + (int64_t)(n0 / 16) * 1024;
     src.wstep = (size_t)N * kBK;
-    make_code_src<C, M32>(src, [&](int r) { return (uint32_t)(min(r, mlast) * lda); },
-                          [&](int qw, int l) { return packed_woff(qw, l, N / 16, C::BN / 16); });
+    make_code_src<C>(src, [&](int r) { return (uint32_t)(min(r, mlast) * lda); },
+                     [&](int qw, int l) { return packed_woff(qw, l, N / 16, C::BN / 16); });
   } else {
     src.wbase = W + (int64_t)n0 * ldw;
     src.wstep = kBK;
-    make_code_src<C, M32>(src, [&](int r) { return (uint32_t)(min(r, mlast) * lda); },
-                          [&](int qw, int l) { return row_major_woff<M32>(qw, l, ldw); });
+    make_code_src<C>(src, [&](int r) { return (uint32_t)(min(r, mlast) * lda); },
+                     [&](int qw, int l) { return row_major_woff(qw, l, ldw); });
   }
   src.scale_dst = -1;
   src.sbase = reinterpret_cast<const uint8_t*>(SA + (int64_t)m0 * nkb);
