@@ -81,7 +81,9 @@ struct Cfg {
   static constexpr int BUF = OFF_SB + (MX ? BN * 4 : 256);
   static_assert(GROUPS % NW == 0, "row groups must split evenly over waves");
   static_assert(NS <= NW, "at most one scale load per wave");
-  static_assert(TM % 16 == 0 && TN % 16 == 0 && BM % 64 == 0 && BN % 128 == 0, "tile shape");
+  static_assert(TM % 16 == 0 && TN % 16 == 0 && BM % 64 == 0 && BN % 64 == 0 && (BN % 128 == 0 || !MX),
+                "tile shape");
+  static_assert(BN % 128 == 0 || 128 % BN == 0, "a tile's weight rows span whole 128-row scale blocks or lie in one");
   static_assert(TN <= 128, "a wave's columns lie in one weight-scale block");
   static_assert(S == 2 || S == 3, "two or three LDS stages");
   static_assert(S * BUF <= 160 * 1024, "LDS capacity");
@@ -482,16 +484,23 @@ __device__ __forceinline__ void k_loop(uint8_t* l0, uint8_t* l1, uint8_t* l2, co
   }
 }
 
-// Four consecutive outputs: bf16 by v_cvt_pk_bf16_f32 (round to nearest
-// even, two values per instruction), or fp32.
-template <bool BF16>
+// Four consecutive outputs as fp32, or as bf16 rounded to nearest even:
+// by v_cvt_pk_bf16_f32 (HW, two values per instruction; the tiled GEMMs'
+// epilogues), or by integer rounding (the streaming kernels, whose
+// registers the hardware form left at occupancy 1 for four subtiles).
+template <bool BF16, bool HW = true>
 __device__ __forceinline__ void store4(void* __restrict__ y, int64_t off, const v4f v) {
   if (BF16) {
-    const bf16x2 b0 = {(__bf16)v[0], (__bf16)v[1]};
-    const bf16x2 b1 = {(__bf16)v[2], (__bf16)v[3]};
     uint2 p;
-    p.x = __builtin_bit_cast(uint32_t, b0);
-    p.y = __builtin_bit_cast(uint32_t, b1);
+    if (HW) {
+      const bf16x2 b0 = {(__bf16)v[0], (__bf16)v[1]};
+      const bf16x2 b1 = {(__bf16)v[2], (__bf16)v[3]};
+      p.x = __builtin_bit_cast(uint32_t, b0);
+      p.y = __builtin_bit_cast(uint32_t, b1);
+    } else {
+      p.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+      p.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+    }
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + off) = p;
   } else {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + off) = make_float4(v[0], v[1], v[2], v[3]);
@@ -738,7 +747,7 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void block_gemm_kernel(
     src.scale_dst = C::OFF_SA + 256 * wave;
   } else if (wave == C::NS_A) {
     src.sbase = reinterpret_cast<const uint8_t*>(SW + (int64_t)(n0 / 128) * nkb);
-    src.soff = (uint32_t)(min(lane, C::BN / 128 - 1) * nkb * 4);
+    src.soff = (uint32_t)(min(lane, (C::BN + 127) / 128 - 1) * nkb * 4);
     src.scale_dst = C::OFF_SB;
   }
 
@@ -1113,7 +1122,7 @@ __device__ __forceinline__ void stream_store(void* __restrict__ y, const v4f (&a
     const int64_t base = row_off(16 * i + l16);
     if (base >= 0) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) store4<BF16>(y, base + n0 + 16 * j + 4 * g, acc[i][j]);
+      for (int j = 0; j < NJ; ++j) store4<BF16, false>(y, base + n0 + 16 * j + 4 * g, acc[i][j]);
     }
   }
 }
@@ -1282,7 +1291,7 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
         src.scale_dst = C::OFF_SA + 256 * wave;
       } else if (wave == C::NS_A) {
         src.sbase = reinterpret_cast<const uint8_t*>(SW + ((int64_t)e * (N / 128) + n0 / 128) * nkb);
-        src.soff = (uint32_t)(min(lane, C::BN / 128 - 1) * nkb * 4);
+        src.soff = (uint32_t)(min(lane, (C::BN + 127) / 128 - 1) * nkb * 4);
         src.scale_dst = C::OFF_SB;
       }
       v4f acc[C::MI][C::NJ];
@@ -1358,7 +1367,10 @@ using BlockCfg = Cfg<FP8B_BLOCK_CFG, false, FP8B_BLOCK_STAGES>;
 // M up to 128 past the streaming kernel: 64 x 128 tiles (4 waves of
 // 64 x 32), twice the tiles of 128 x 128 so a decode-sized layer fills the
 // chip (measured at 8192 -> 28672: M 64 93 -> 72 us, M 128 95 -> 89 us;
-// three stages were slower).
+// three stages were slower).  128 x 64 tiles, which hold every token row
+// of M = 128 in one tile, measured slower (85.7 against 78.6 us at M 128):
+// the two m-tiles of a 64 x 128 column meet in one XCD's L2, so the weights
+// are not streamed twice from HBM.
 #ifndef FP8B_SMALL_CFG
 #define FP8B_SMALL_CFG 64, 128, 1, 4, false, 2
 #endif

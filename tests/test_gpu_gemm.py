@@ -151,17 +151,22 @@ def test_linear_step_graph_replay_matches_eager(F, M):
 
 
 def test_block_gemm_decode_full(F, orc):
+    """8192 -> 28672 at every decode size and across the path switches
+    (streaming up to 64 tokens, 64 x 128 tiles up to 128), both weight
+    layouts; sampled token rows x every output column."""
     c = W.decode_linear(device=DEV)
     a, sa = F.fp8_act_quant(c.x, 128, "ue8m0")
     wq, ws = F.fp8_weight_quant(c.w, "ue8m0")
+    wp = F.fp8_weight_pack(wq)
     ow, osw = orc.weight_quant(W.bits(c.w), 1)
-    for M in (1, 8, 32, 48, 64, 128):
-        y = F.fp8_block_gemm(a[:M], sa[:M], wq, ws, torch.bfloat16)
-        torch.cuda.synchronize()
+    for M in (1, 8, 32, 48, 64, 65, 100, 128):
         rows = sorted({0, M - 1, M // 2})
         oa, osa = orc.act_quant(W.bits(c.x[rows]), 128, 1)
         yr, bnd = orc.block_gemm(oa, osa, ow, osw)
-        assert_parity(_np(y[rows]), yr, bnd, True, f"decode M={M}")
+        for name, y in (("row-major", F.fp8_block_gemm(a[:M], sa[:M], wq, ws, torch.bfloat16)),
+                        ("packed", F.fp8_block_gemm_packed(a[:M], sa[:M], wp, ws, torch.bfloat16))):
+            torch.cuda.synchronize()
+            assert_parity(_np(y[rows]), yr, bnd, True, f"decode M={M} {name}")
 
 
 def test_block_gemm_prefill_full_sampled(F, orc):
