@@ -1379,11 +1379,22 @@ using MxCfg = Cfg<FP8B_MX_CFG, true, FP8B_MX_STAGES>;
 using MxSmallCfg = Cfg<128, 128, 2, 2, true, 2>;
 using GroupedCfg = Cfg<128, 128, 2, 2, false, 2>;
 
-static int cu_count() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    return 256;
+// Compute units of the device a stream launches on, queried once per device
+// and cached (relaxed atomics: racing first calls store the same value).
+constexpr int kMaxDevices = 64;
+static int cu_count(hipStream_t s) {
+  static int cached[kMaxDevices];  // 0 = not queried yet
+  hipDevice_t dev = 0;
+  if (s == nullptr || hipStreamGetDevice(s, &dev) != hipSuccess) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return 256;
+    dev = cur;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  int n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  __atomic_store_n(&cached[dev], n, __ATOMIC_RELAXED);
   return n;
 }
 
@@ -1514,7 +1525,7 @@ int launch_grouped_gemm(const uint8_t* a, const float* sa, int64_t T, const int3
   // enough persistent workgroups to fill every CU (at its occupancy), never
   // more than the largest possible number of tiles
   const int64_t max_tiles = ((R + C::BM - 1) / C::BM + E) * (N / C::BN) + E * (N / kStreamRows);
-  const int64_t nwg = std::max<int64_t>(1, std::min<int64_t>((512 / C::NT) * (int64_t)cu_count(), max_tiles));
+  const int64_t nwg = std::max<int64_t>(1, std::min<int64_t>((512 / C::NT) * (int64_t)cu_count(s), max_tiles));
   const dim3 grid((unsigned)nwg), block(C::NT);
 #define FP8B_GROUPED(BF, PK)                                                                                  \
   hipLaunchKernelGGL((grouped_gemm_kernel<C, BF, PK>), grid, block, 0, s, a, sa, (int)T, ri, offs, (int)R, \

@@ -34,10 +34,11 @@ _i64 = ctypes.c_int64
 
 
 def lib():
-    """Load (building first if absent) the oracle shared library."""
+    """Load (building first if absent) the oracle shared library, or the one
+    FP8_ORACLE_LIB names (the sanitizer build of the same source)."""
     global _LIB
     if _LIB is None:
-        path = _build.LIB
+        path = os.environ.get("FP8_ORACLE_LIB") or _build.LIB
         if not os.path.exists(path):
             _build.build()
         L = ctypes.CDLL(path)

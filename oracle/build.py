@@ -13,11 +13,24 @@ LIB = os.path.join(HERE, "libfp8_oracle.so")
 SRC = os.path.join(HERE, "fp8_oracle.c")
 
 
+FLAGS = ["-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra"]
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
+def build_sanitized(out: str, verbose: bool = False) -> str:
+    """The same oracle built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (any report aborts), for running the oracle's pins under them; load it
+    with libasan preloaded and FP8_ORACLE_LIB pointing at `out`."""
+    cmd = ["gcc", "-O1"] + FLAGS + SANITIZE + ["-o", out, SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    return out
+
+
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
-    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared",
-           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
-           "-o", tmp, SRC, "-lm"]
+    cmd = ["gcc", "-O2"] + FLAGS + ["-o", tmp, SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
