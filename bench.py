@@ -263,8 +263,13 @@ def main():
     t_gemm = sum(gemm_ms) / len(gemm_ms) * 1e-3
     t_gemm_median = statistics.median(gemm_ms) * 1e-3
 
-    # act_quant alone: 17 us, so timed back to back from a captured graph
+    # act_quant alone: 17 us, so timed back to back from a captured graph;
+    # beside it, the same launch with the arithmetic removed (the same bytes
+    # moved) and an empty launch of the same grid (fp8b_stream_probe)
     t_aq = timed_graph(torch, aq, max(args.steps, 10))
+    t_copy = timed_graph(torch, lambda: F.fp8b_stream_probe(F.PROBE_COPY, x, a, sa), max(args.steps, 10))
+    t_empty = timed_graph(torch, lambda: F.fp8b_stream_probe(F.PROBE_EMPTY, x, a, sa), max(args.steps, 10))
+    aq()                                   # restore the step's codes and scales
     gemm_bytes = M * K + N * K + M * (K // 128) * 4 + (N // 128) * (K // 128) * 4 + M * N * 2
     aq_bytes = M * K * 2 + M * K + M * (K // 128) * 4
     achieved = flops / t_gemm / 1e12
@@ -279,6 +284,12 @@ def main():
     legs["prefill"] = {"act_quant_us": round(t_aq * 1e6, 2),
                        "act_quant_GBps": round(aq_bytes / t_aq / 1e9, 1),
                        "act_quant_hbm_frac": round(aq_bytes / t_aq / 1e9 / PEAK_HBM_GBS, 4),
+                       "act_quant_probe": {"copy_us": round(t_copy * 1e6, 2),
+                                           "copy_GBps": round(aq_bytes / t_copy / 1e9, 1),
+                                           "empty_us": round(t_empty * 1e6, 2),
+                                           "act_quant_vs_copy": round(t_copy / t_aq, 4),
+                                           "note": "same grid, loads and stores as act_quant: copy moves the "
+                                                   "same bytes with no arithmetic, empty returns at once"},
                        "gemm_us": round(t_gemm * 1e6, 2), "gemm_TFLOPs": round(achieved, 1),
                        "weights": "packed layout (fp8_weight_pack, offline)"}
     del c

@@ -25,6 +25,7 @@ SCALE_FP32, SCALE_UE8M0, SCALE_E8M0_BYTE = 0, 1, 2
 OUT_F32, OUT_BF16 = 0, 1
 FMT_E4M3, FMT_E5M2 = 0, 1
 MFMA_BF16_16X16X32, MFMA_FP8_16X16X128 = 0, 1
+PROBE_COPY, PROBE_EMPTY = 0, 1
 MFMA_LOOP_FLOPS = {MFMA_BF16_16X16X32: 16384, MFMA_FP8_16X16X128: 65536}   # per MFMA instruction
 DELAYED_HEADER_BYTES = 128 + 128 * 16    # FP8B_DELAYED_HEADER_BYTES of include/fp8blk.h
 
@@ -85,6 +86,8 @@ def lib():
         L.fp8_delayed_quant.argtypes = [vp, i64, vp, i64, ci, ctypes.c_float, vp, vp, vp]
         L.fp8_cast_f32.restype = ci
         L.fp8_cast_f32.argtypes = [vp, i64, ci, vp, vp]
+        L.fp8b_stream_probe.restype = ci
+        L.fp8b_stream_probe.argtypes = [ci, vp, i64, i64, vp, vp, vp]
         L.fp8b_mfma_loop.restype = ci
         L.fp8b_mfma_loop.argtypes = [ci, vp, i64, i64, vp, vp]
         _lib = L
@@ -496,3 +499,21 @@ def fp8b_mfma_loop(kind: int, ops: torch.Tensor, iters: int, workgroups: int, ou
     rc = lib().fp8b_mfma_loop(int(kind), _p(ops), int(iters), int(workgroups), _p(out), _stream(ops))
     _check("fp8b_mfma_loop", rc)
     return out
+
+
+def fp8b_stream_probe(kind: int, x: torch.Tensor, q: torch.Tensor, scales: torch.Tensor):
+    """The act_quant launch with its arithmetic removed (a measurement aid,
+    not a step of the method): PROBE_COPY moves the same bytes (q = low byte
+    of each bf16, scales = 0), PROBE_EMPTY launches the same grid and does
+    nothing.  x bf16 [M, K], q uint8 [M, K], scales float32 [M, K/128], all
+    contiguous on one GPU."""
+    _need(x.dtype == torch.bfloat16 and x.dim() == 2 and x.is_contiguous(), "x must be contiguous 2-D bf16")
+    M, K = x.shape
+    _need(q.dtype == torch.uint8 and q.is_contiguous(), "q must be contiguous uint8")
+    _shape(q, (M, K), "q")
+    _need(scales.dtype == torch.float32 and scales.is_contiguous(), "scales must be contiguous float32")
+    _shape(scales, (M, K // 128), "scales")
+    _on_gpu(x, q, scales)
+    rc = lib().fp8b_stream_probe(int(kind), _p(x), M, K, _p(q), _p(scales), _stream(x))
+    _check("fp8b_stream_probe", rc)
+    return q

@@ -230,6 +230,16 @@ FP8B_EXPORT int fp8_cast_f32(const float* x, int64_t n, int fmt, uint8_t* q, voi
   return fp8blk::launch_cast(x, n, fmt, q, as_stream(stream));
 }
 
+FP8B_EXPORT int fp8b_stream_probe(int kind, const void* x, int64_t M, int64_t K, uint8_t* q, float* scales,
+                                  void* stream) {
+  if (kind != FP8B_PROBE_COPY && kind != FP8B_PROBE_EMPTY) return FP8B_EUNSUPPORTED;
+  if (!x || !q || !scales) return FP8B_EINVAL;
+  if (M < 1 || K <= 0 || M > kMaxDim || K > kMaxDim || K % 128 != 0) return FP8B_EINVAL;
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scales, 4)) return FP8B_EALIGN;
+  if (M * (K / 8) / 512 >= INT32_MAX) return FP8B_EINVAL;
+  return fp8blk::launch_stream_probe(kind, x, M, K, q, scales, as_stream(stream));
+}
+
 FP8B_EXPORT int fp8b_mfma_loop(int kind, const uint32_t* ops, int64_t iters, int64_t workgroups, float* out,
                                void* stream) {
   if (kind != FP8B_MFMA_BF16_16X16X32 && kind != FP8B_MFMA_FP8_16X16X128) return FP8B_EUNSUPPORTED;

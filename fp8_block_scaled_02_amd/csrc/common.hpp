@@ -22,6 +22,31 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Maxima of non-negative floats (block amax values) on their bit patterns,
+// which order like unsigned integers: one v_max_u32 with a DPP operand per
+// step and no float canonicalisation.  row16: quad swaps, then half-row and
+// row mirrors (every lane of a 16-lane row ends with the row maximum); quad:
+// each aligned quad of lanes.
+template <int CTRL>
+__device__ __forceinline__ uint32_t umax_dpp(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ float row16_max_nonneg(float v) {
+  uint32_t u = __float_as_uint(v);
+  u = umax_dpp<0xB1>(u);
+  u = umax_dpp<0x4E>(u);
+  u = umax_dpp<0x141>(u);
+  u = umax_dpp<0x140>(u);
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ float quad_max_nonneg(float v) {
+  uint32_t u = __float_as_uint(v);
+  u = umax_dpp<0xB1>(u);
+  u = umax_dpp<0x4E>(u);
+  return __uint_as_float(u);
+}
+
 // max over the 16 lanes of a DPP row (quad swaps, then half-row and row
 // mirrors); every lane of the row ends with the row maximum.
 __device__ __forceinline__ float row16_max(float v) {
@@ -77,18 +102,17 @@ __device__ __forceinline__ float clamp448(float v) {
 
 // Division by a block scale d = fp32(amax / Fmax) (Fmax 448 for E4M3 codes,
 // 57344 for E5M2), correctly rounded like the IEEE quotient x / d, at a
-// fraction of its cost.  Per block: y = 1 / d
-// (one IEEE division).  Per element: q = x * y, one residual r = x - q * d
-// (exact with FMA) and one correction q + r * y (Markstein's method for a
-// correctly rounded reciprocal), then the sign of x restored (the
-// correction turns (-0) into +0).  Blocks with amax < 2^-62 would put the
-// residual below fp32's normal range and use the IEEE division instead.
-// (With amax >= 2^-62 the residual of every quotient that can round to a
-// nonzero code, E4M3 or E5M2, is a normal fp32.)  Verified exhaustively on
-// gfx950 for E4M3: for every positive finite bf16 amax and every bf16 x with
-// |x| <= amax, the code of the clamped quotient is identical to the one from
-// the IEEE division; the parity tests run one block per bf16 amax for both
-// formats.
+// fraction of its cost.  Per block: y ~ 1 / d (a reciprocal estimate and one
+// Newton step).  Per element: q = x * y, one residual r = x - q * d (exact
+// with FMA) and one correction q + r * y (Markstein's method), then the sign
+// of x restored (the correction turns (-0) into +0).  Blocks with
+// amax < 2^-62 would put the residual below fp32's normal range and use the
+// IEEE division instead.  (With amax >= 2^-62 the residual of every quotient
+// that can round to a nonzero code, E4M3 or E5M2, is a normal fp32.)  The
+// GPU sweep tests run every positive finite bf16 amax with every bf16 x with
+// |x| <= amax through act_quant (E4M3) and the KV quantiser (E5M2) and
+// require the oracle's codes -- which, since inputs are bf16, covers every
+// (amax, x) pair these kernels can see.
 struct BlockDivisor {
   float d, y;
   bool fast;
@@ -98,8 +122,26 @@ __device__ __forceinline__ BlockDivisor make_divisor(float amax, float d) {
   BlockDivisor b;
   b.d = d;
   b.fast = amax >= 0x1.0p-62f;
-  b.y = 1.0f / d;
+  // reciprocal estimate refined by one Newton step (d is normal on the fast
+  // path); the per-element correction then rounds the quotient correctly,
+  // which the exhaustive sweep (every bf16 amax with every |x| <= amax)
+  // checks against the IEEE division on gfx950
+  const float y0 = __builtin_amdgcn_rcpf(d);
+  b.y = __builtin_fmaf(__builtin_fmaf(-d, y0, 1.0f), y0, y0);
   return b;
+}
+
+// d = fp32(amax / fmax) for a positive finite amax, without an IEEE
+// division: d0 = RN(amax * c) with c = RN(1 / fmax), the exact residual
+// r = amax - d0 * fmax (FMA), then d = RN(d0 + r * c) -- one correction
+// step (Markstein's method).  Verified in exact rational arithmetic for
+// every positive finite bf16 amax with fmax = 448 and 57344 (the only
+// values amax takes here, the maximum of bf16 inputs); amax = 0 gives 1.
+__device__ __forceinline__ float block_scale(float amax, float fmax, float c) {
+  const float d0 = amax * c;
+  const float r = __builtin_fmaf(-d0, fmax, amax);
+  const float d = __builtin_fmaf(r, c, d0);
+  return amax == 0.0f ? 1.0f : d;
 }
 
 __device__ __forceinline__ float divide(float x, const BlockDivisor& b) {
@@ -107,6 +149,27 @@ __device__ __forceinline__ float divide(float x, const BlockDivisor& b) {
   const float q = x * b.y;
   const float r = __builtin_fmaf(-q, b.d, x);
   return copysignf(__builtin_fmaf(r, b.y, q), x);
+}
+
+// The same quotient for N values of one block, with the fast / IEEE choice
+// taken once for the block (a branch per element cost more than the
+// quotient itself).
+template <int N>
+__device__ __forceinline__ void divide_block(const float (&x)[N], float (&q)[N], const BlockDivisor& b) {
+  if (b.fast) {
+    // with the residual negated, r' = t * d - x and q = t - r' * y, the
+    // zero cases keep the sign of x (x = -0: r' = +0 and q = -0 + -0 = -0)
+    // with no copysign; the negations are free source modifiers
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const float t = x[i] * b.y;
+      const float rn = __builtin_fmaf(t, b.d, -x[i]);
+      q[i] = __builtin_fmaf(-rn, b.y, t);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) q[i] = x[i] / b.d;
+  }
 }
 
 }  // namespace fp8blk

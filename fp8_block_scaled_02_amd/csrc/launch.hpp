@@ -13,6 +13,8 @@ inline int check_launch() {
 
 int launch_act_quant(const void* x, int64_t M, int64_t K, int64_t ldx, int block, int fmt,
                      uint8_t* q, int64_t ldq, void* scales, hipStream_t s);
+int launch_stream_probe(int kind, const void* x, int64_t M, int64_t K, uint8_t* q, float* scales,
+                        hipStream_t s);
 int launch_weight_quant(const void* w, int64_t N, int64_t K, int64_t ldw, int fmt, uint8_t* q,
                         int64_t ldq, float* scales, hipStream_t s);
 int launch_cast(const float* x, int64_t n, int fmt, uint8_t* q, hipStream_t s);

@@ -23,10 +23,16 @@ namespace fp8blk {
 // row (so no index needs a division); each thread owns UNROLL chunks 256
 // apart, all loaded before any is processed (bytes in flight per lane =
 // 16 * UNROLL).
-template <int BLOCK, int FMT, int UNROLL>
+//
+// PROBE (a measurement aid, fp8b_stream_probe): 1 moves the same bytes with
+// the same grid, loads and stores but no arithmetic (each code byte is the
+// low byte of its bf16 element, each scale 0); 2 returns at once (the
+// launch and drain of the same grid).
+template <int BLOCK, int FMT, int UNROLL, int PROBE = 0>
 __global__ __launch_bounds__(256) void act_quant_kernel(
     const uint16_t* __restrict__ x, int64_t K, int64_t ldx,
     uint8_t* __restrict__ q, int64_t ldq, void* __restrict__ scales) {
+  if (PROBE == 2) return;
   constexpr int LPB = BLOCK / 8;  // lanes per quantisation block
   const int cpr = (int)(K / 8);   // 16-byte chunks per row
   const int nblk = (int)(K / BLOCK);
@@ -43,6 +49,20 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
     if (c < cpr) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + 8 * c));
     raw[u] = make_uint4(v[0], v[1], v[2], v[3]);
   }
+  if (PROBE == 1) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int c = base + u * 256;
+      if (c < cpr) {
+        u32x2 out;
+        out[0] = __builtin_amdgcn_perm(raw[u].y, raw[u].x, 0x06040200u);
+        out[1] = __builtin_amdgcn_perm(raw[u].w, raw[u].z, 0x06040200u);
+        __builtin_nontemporal_store(out, reinterpret_cast<u32x2*>(qr + 8 * c));
+        if ((c % LPB) == 0) reinterpret_cast<float*>(scales)[row * nblk + c / LPB] = 0.0f;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
     const int c = base + u * 256;
@@ -56,17 +76,18 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-    amax = (LPB == 16) ? row16_max(amax) : quad_max(amax);
+    amax = (LPB == 16) ? row16_max_nonneg(amax) : quad_max_nonneg(amax);
 
     float qv[8];
     const bool ok = c < cpr;
     const bool lead = ok && (c % LPB) == 0;
     const int64_t sidx = row * nblk + c / LPB;
     if (FMT == 0) {
-      const float d = (amax == 0.0f) ? 1.0f : amax / 448.0f;  // IEEE division
+      const float d = block_scale(amax, 448.0f, 1.0f / 448.0f);
       const BlockDivisor bd = make_divisor(amax, d);
+      divide_block(f, qv, bd);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qv[i] = clamp448(divide(f[i], bd));
+      for (int i = 0; i < 8; ++i) qv[i] = clamp448(qv[i]);
       if (lead) reinterpret_cast<float*>(scales)[sidx] = d;
     } else {
       const int e = pow2_scale_exp(amax);
@@ -130,7 +151,7 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(
   float d, rinv = 1.0f;
   BlockDivisor bd{};
   if (FMT == 0) {
-    d = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+    d = block_scale(amax, 448.0f, 1.0f / 448.0f);
     bd = make_divisor(amax, d);
   } else {
     const int e = pow2_scale_exp(amax);
@@ -149,8 +170,14 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(
       f[2 * j] = bf16_bits_to_f32(v[j] & 0xffffu);
       f[2 * j + 1] = bf16_bits_to_f32(v[j] >> 16);
     }
+    if (FMT == 0) {
+      divide_block(f, f, bd);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) f[j] = clamp448(FMT == 0 ? divide(f[j], bd) : f[j] * rinv);
+      for (int j = 0; j < 8; ++j) f[j] *= rinv;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = clamp448(f[j]);
     uint2 out;
     out.x = pack4_e4m3(f[0], f[1], f[2], f[3]);
     out.y = pack4_e4m3(f[4], f[5], f[6], f[7]);
@@ -231,7 +258,7 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(
   amax = row16_max(amax);
   amax = fmaxf(amax, __shfl_xor(amax, 16));
   amax = fmaxf(amax, __shfl_xor(amax, 32));
-  const float d = (amax == 0.0f) ? 1.0f : amax / 57344.0f;  // IEEE division
+  const float d = block_scale(amax, 57344.0f, 1.0f / 57344.0f);
   const BlockDivisor bd = make_divisor(amax, d);
   if (lane == 0) scales[t] = d;
 #pragma unroll
@@ -239,12 +266,15 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(
     const int64_t c = lane + 64 * u;
     if (c >= nch) continue;
     const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
-    float v[8];
+    float f[8], v[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v[2 * i] = fminf(fmaxf(divide(bf16_bits_to_f32(w[i] & 0xffffu), bd), -57344.0f), 57344.0f);
-      v[2 * i + 1] = fminf(fmaxf(divide(__uint_as_float(w[i] & 0xffff0000u), bd), -57344.0f), 57344.0f);
+      f[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
+    divide_block(f, v, bd);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = fminf(fmaxf(v[i], -57344.0f), 57344.0f);
     u32x2 out;
     out[0] = pack4_e5m2(v[0], v[1], v[2], v[3]);
     out[1] = pack4_e5m2(v[4], v[5], v[6], v[7]);
@@ -514,6 +544,20 @@ int launch_act_quant(const void* x, int64_t M, int64_t K, int64_t ldx, int block
     else FP8B_AQ(32, 2);
   }
 #undef FP8B_AQ
+  return check_launch();
+}
+
+int launch_stream_probe(int kind, const void* x, int64_t M, int64_t K, uint8_t* q, float* scales,
+                        hipStream_t s) {
+  const int64_t cpr = K / 8;
+  const int64_t segs = (cpr + 256 * kActUnroll - 1) / (256 * kActUnroll);
+  if (segs > 65535 || M > 0x7fffffff) return FP8B_EINVAL;
+  const dim3 grid((unsigned)M, (unsigned)segs);
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  if (kind == 0)
+    hipLaunchKernelGGL((act_quant_kernel<128, 0, kActUnroll, 1>), grid, dim3(256), 0, s, xp, K, K, q, K, scales);
+  else
+    hipLaunchKernelGGL((act_quant_kernel<128, 0, kActUnroll, 2>), grid, dim3(256), 0, s, xp, K, K, q, K, scales);
   return check_launch();
 }
 

@@ -432,6 +432,26 @@ typedef enum { FP8B_MFMA_BF16_16X16X32 = 0, FP8B_MFMA_FP8_16X16X128 = 1 } fp8b_m
 int fp8b_mfma_loop(int kind, const uint32_t *ops, int64_t iters, int64_t workgroups,
                    float *out, void *stream);
 
+/*
+ * fp8b_stream_probe -- a measurement aid, not a step of the method: the
+ * launch of fp8_act_quant (block 128, fp32 scales) on x bf16 [M][K]
+ * (contiguous rows) with the same grid, loads and stores, but
+ *   FP8B_PROBE_COPY:  no arithmetic -- q[m][k] = low byte of x[m][k] and
+ *                     scales[m][k/128] = 0 (the same bytes moved);
+ *   FP8B_PROBE_EMPTY: every workgroup returns at once (launch and drain).
+ * Timed beside fp8_act_quant it separates the memory system's rate for this
+ * access pattern, and the launch's fixed cost, from the quantiser's own work.
+ *
+ *   x        bf16 [M][K], 16-byte aligned; M >= 1; K > 0, K % 128 == 0.
+ *   q        uint8 [M][K], 8-byte aligned.
+ *   scales   float [M][K/128], 4-byte aligned.
+ *   Returns FP8B_EUNSUPPORTED for another kind.
+ */
+typedef enum { FP8B_PROBE_COPY = 0, FP8B_PROBE_EMPTY = 1 } fp8b_probe_kind;
+
+int fp8b_stream_probe(int kind, const void *x, int64_t M, int64_t K,
+                      uint8_t *q, float *scales, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

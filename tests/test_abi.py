@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
         "fp8b_abi_version", "fp8b_status_string", "fp8_act_quant", "fp8_weight_quant",
         "fp8_block_gemm", "mxfp8_gemm", "fp8_grouped_gemm", "fp8_moe_combine", "fp8_weight_dequant", "fp8_kv_quant", "fp8_kv_dequant",
         "fp8_delayed_state_init", "fp8_delayed_quant", "fp8_cast_f32",
-        "fp8_weight_pack", "fp8_block_gemm_packed", "fp8_grouped_gemm_packed", "fp8b_mfma_loop"])
+        "fp8_weight_pack", "fp8_block_gemm_packed", "fp8_grouped_gemm_packed", "fp8b_mfma_loop",
+        "fp8b_stream_probe"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -226,6 +227,15 @@ def test_mfma_loop_validation(L):
     assert f(0, GOOD, 1, 0, GOOD, NULL) == -1              # workgroups < 1
     assert f(1, GOOD, 1, (1 << 20) + 1, GOOD, NULL) == -1
     assert f(0, ODD, 1, 1, GOOD, NULL) == -2               # ops not 16-byte aligned
+
+
+def test_stream_probe_validation(L):
+    f = L.fp8b_stream_probe
+    assert f(2, GOOD, 4, 256, GOOD, GOOD, NULL) == -3       # unknown kind
+    assert f(0, NULL, 4, 256, GOOD, GOOD, NULL) == -1
+    assert f(0, GOOD, 0, 256, GOOD, GOOD, NULL) == -1       # M < 1
+    assert f(1, GOOD, 4, 200, GOOD, GOOD, NULL) == -1       # K % 128
+    assert f(0, ODD, 4, 256, GOOD, GOOD, NULL) == -2
 
 
 def test_binding_rejects_cpu_misuse():

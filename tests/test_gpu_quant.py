@@ -471,3 +471,21 @@ def test_act_quant_many_short_rows(F, orc):
     g = W.gen(45)
     x = W.activations(70000, 128, 1, 30.0, g)
     _assert_same(*_run_act(F, orc, x, 128, "fp32"), "70000x128")
+
+
+def test_stream_probe_moves_the_act_quant_bytes(F):
+    """The act_quant measurement probe: the copy kind writes each bf16's low
+    byte as its code and zero scales (every row, including a partial last
+    workgroup of chunks); the empty kind writes nothing."""
+    g = W.gen(70)
+    x = W.activations(37, 7168, 4, 20.0, g).to(DEV)
+    q = torch.full((37, 7168), 0xAB, dtype=torch.uint8, device=DEV)
+    sc = torch.full((37, 56), 7.0, dtype=torch.float32, device=DEV)
+    F.fp8b_stream_probe(F.PROBE_EMPTY, x, q, sc)
+    torch.cuda.synchronize()
+    assert (_np(q) == 0xAB).all() and (_np(sc) == 7.0).all()
+    F.fp8b_stream_probe(F.PROBE_COPY, x, q, sc)
+    torch.cuda.synchronize()
+    low = W.bits(x).astype(np.uint16) & 0xFF
+    assert np.array_equal(_np(q), low.astype(np.uint8)) and (_np(sc) == 0.0).all()
+
