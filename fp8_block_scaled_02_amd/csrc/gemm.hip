@@ -68,6 +68,7 @@ struct Cfg {
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
   static constexpr int MI = TM / 16, NJ = TN / 16;  // 16x16 subtiles per wave
+  static constexpr int MI32 = TM / 32, NJ32 = TN / 32;  // 32x32 blocks per wave (32 x 32 K step)
   static constexpr int GROUPS = (BM + BN) / 8;      // 1 KB row groups per K step
   static constexpr int NI = GROUPS / NW;            // code DMA instructions per wave
   // scale DMA instructions per K step (64 lanes x 4 bytes each)
@@ -570,38 +571,43 @@ __device__ __forceinline__ int w32_at(int off, int kk2) {
 
 // One K block: accumulate this block's partials into P (its scales into sn)
 // while folding the previous block's partials Pp (scales sp) into acc: in
-// MFMA window kk every chain folds its values 2kk, 2kk+1, so the 64 FMAs
-// of a block issue beside its 32 MFMAs instead of in one burst (empty asm
-// statements tie each window's folds to the next window's operands).
+// MFMA window kk every chain folds its values 2kk, 2kk+1, so the FMAs of a
+// block issue beside its MFMAs instead of in one burst (empty asm statements
+// tie each window's folds to the next window's operands).  A wave holds
+// MI32 x NJ32 blocks of 32 x 32 (2 x 2 for 64 x 64 wave tiles, 2 x 1 for
+// 64 x 32).
+template <class C>
+using Acc32 = v16f[C::MI32][C::NJ32];
+
 template <class C, bool PK, class Hook>
-__device__ __forceinline__ void compute_block32(const uint8_t* buf, v16f (&acc)[2][2], v16f (&P)[2][2],
-                                                const v16f (&Pp)[2][2], const float (&sp)[2], float (&sn)[2],
-                                                Hook hook) {
-  static_assert(C::TM == 64 && C::TN == 64, "2 x 2 blocks of 32 x 32 per wave");
+__device__ __forceinline__ void compute_block32(const uint8_t* buf, Acc32<C>& acc, Acc32<C>& P, const Acc32<C>& Pp,
+                                                const float (&sp)[C::MI32], float (&sn)[C::MI32], Hook hook) {
+  constexpr int MI = C::MI32, NJ = C::NJ32;
+  static_assert(C::TM == 32 * MI && C::TN == 32 * NJ && MI <= 2 && NJ <= 2, "32 x 32 blocks per wave");
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave % C::WM, wn = wave / C::WM, r = lane & 31, h = lane >> 5;
   const float* sa = reinterpret_cast<const float*>(buf + C::OFF_SA);
   const float* sw = reinterpret_cast<const float*>(buf + C::OFF_SB);
   const uint8_t* wt = buf + C::OFF_W;
-  uint4 ra[2][2], rw[2][2];  // [slot][fragment]: 16 code bytes = MFMAs 2kk2, 2kk2+1
+  uint4 ra[2][MI], rw[2][NJ];  // [slot][fragment]: 16 code bytes = MFMAs 2kk2, 2kk2+1
   // chunk 4h + kk2 of a swizzled row sits at lds_off(row, 4h) ^ (kk2 << 4)
   // (kk2 < 4 only flips bits 4-5 of the chunk offset)
-  const int a_off = lds_off(wm * 64 + r, 4 * h);  // fragment 1 is 32 rows (4096 bytes) further
-  const int w_off = w32_off<C, PK>(wn * 64 + r, h);
+  const int a_off = lds_off(wm * C::TM + r, 4 * h);  // fragment 1 is 32 rows (4096 bytes) further
+  const int w_off = w32_off<C, PK>(wn * C::TN + r, h);
   // fragment 1 is 32 rows further: two packed chunks (2048 bytes) or 4096 bytes of rows
   constexpr int w_frag = PK ? 2048 : 4096;
   auto load = [&](int sl, int kk2) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
       ra[sl][i] = *reinterpret_cast<const uint4*>(buf + 4096 * i + (a_off ^ (kk2 << 4)));
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
       rw[sl][j] = *reinterpret_cast<const uint4*>(wt + w_frag * j + w32_at<PK>(w_off, kk2));
   };
   load(0, 0);
-  const float swv = sw[(wn * 64) / 128];
+  const float swv = sw[(wn * C::TN) / 128];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) sn[i] = sa[wm * 64 + 32 * i + r] * swv;
+  for (int i = 0; i < MI; ++i) sn[i] = sa[wm * C::TM + 32 * i + r] * swv;
   hook();
 #pragma unroll
   for (int kk2 = 0; kk2 < 4; ++kk2) {
@@ -610,17 +616,17 @@ __device__ __forceinline__ void compute_block32(const uint8_t* buf, v16f (&acc)[
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int kk = 2 * kk2 + half;
-      bf16x8 xa[2], xw[2];
+      bf16x8 xa[MI], xw[NJ];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
         xa[i] = half ? cvt8(ra[sl][i].z, ra[sl][i].w, 1.0f) : cvt8(ra[sl][i].x, ra[sl][i].y, 1.0f);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ; ++j)
         xw[j] = half ? cvt8(rw[sl][j].z, rw[sl][j].w, 1.0f) : cvt8(rw[sl][j].x, rw[sl][j].y, 1.0f);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           P[i][j] = mfma32_bf16(xw[j], xa[i], kk == 0 ? v16f{} : P[i][j]);
 #pragma unroll
           for (int v = 2 * kk; v < 2 * kk + 2; ++v) acc[i][j][v] = __builtin_fmaf(Pp[i][j][v], sp[i], acc[i][j][v]);
@@ -628,26 +634,41 @@ __device__ __forceinline__ void compute_block32(const uint8_t* buf, v16f (&acc)[
       if (kk < 7) {
         // this window's folds complete before the next window's operands
         // exist (keeps them spread over the block)
-        asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]));
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(acc[i][j]));
       }
     }
   }
 }
 
+template <class C>
+__device__ __forceinline__ void fold32(Acc32<C>& acc, const Acc32<C>& P, const float (&s)[C::MI32]) {
+#pragma unroll
+  for (int i = 0; i < C::MI32; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NJ32; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(P[i][j][v], s[i], acc[i][j][v]);
+}
+
 template <class C, bool PK>
-__device__ __forceinline__ void k_loop32(uint8_t* l0, uint8_t* l1, const Src<C>& src, int nkb, v16f (&acc)[2][2]) {
+__device__ __forceinline__ void k_loop32(uint8_t* l0, uint8_t* l1, const Src<C>& src, int nkb, Acc32<C>& acc) {
   static_assert(C::S == 2, "two LDS stages");
   // partials of the even and odd K blocks; the fold of the block before the
   // first is a no-op on zeros
-  v16f P0[2][2], P1[2][2];
-  float s0[2] = {0.0f, 0.0f}, s1[2] = {0.0f, 0.0f};
+  Acc32<C> P0, P1;
+  float s0[C::MI32], s1[C::MI32];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::MI32; ++i) {
+    s0[i] = s1[i] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < C::NJ32; ++j) {
       acc[i][j] = v16f{};
       P1[i][j] = v16f{};
     }
+  }
   issue<C>(l0, src, 0);
   auto sync = [&]() {
     wait_vmem<0>();
@@ -666,35 +687,25 @@ __device__ __forceinline__ void k_loop32(uint8_t* l0, uint8_t* l1, const Src<C>&
   if (kb < nkb) {  // an odd last block: its partials end in P0
     sync();
     compute_block32<C, PK>(l0, acc, P0, P1, s1, s0, []() {});
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(P0[i][j][v], s0[i], acc[i][j][v]);
+    fold32<C>(acc, P0, s0);
   } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(P1[i][j][v], s1[i], acc[i][j][v]);
+    fold32<C>(acc, P1, s1);
   }
 }
 
 template <class C, bool BF16, class RowOff>
-__device__ __forceinline__ void epilogue32(void* __restrict__ y, const v16f (&acc)[2][2], int n0, RowOff row_off) {
+__device__ __forceinline__ void epilogue32(void* __restrict__ y, const Acc32<C>& acc, int n0, RowOff row_off) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave % C::WM, wn = wave / C::WM, r = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t base = row_off(wm * 64 + 32 * i + r);
+  for (int i = 0; i < C::MI32; ++i) {
+    const int64_t base = row_off(wm * C::TM + 32 * i + r);
     if (base >= 0) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < C::NJ32; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          store4<BF16>(y, base + n0 + wn * 64 + 32 * j + 8 * q + 4 * h,
+          store4<BF16>(y, base + n0 + wn * C::TN + 32 * j + 8 * q + 4 * h,
                        v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]});
     }
   }
@@ -752,7 +763,7 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void block_gemm_kernel(
   }
 
   if constexpr (M32) {
-    v16f acc[2][2];
+    Acc32<C> acc;
     k_loop32<C, PK>(lds0, lds1, src, nkb, acc);
     epilogue32<C, BF16>(Y, acc, n0, [&](int r) -> int64_t { return m0 + r < M ? (int64_t)(m0 + r) * ldy : -1; });
   } else {
@@ -1354,6 +1365,12 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
 #ifndef FP8B_BLOCK_STAGES
 #define FP8B_BLOCK_STAGES 2
 #endif
+// The 64 x 128 small-M tiles stay on the 16 x 16 K step: on the 32 x 32 step
+// (2 x 1 blocks per 64 x 32 wave) 8192 -> 28672 measured 68.4 / 64.9 us
+// against 73.2 / 71.8 at M = 100 / 65, but 79.1 against 77.2 at M = 128.
+#ifndef FP8B_SMALL_MMA32
+#define FP8B_SMALL_MMA32 0
+#endif
 #ifndef FP8B_BLOCK_MMA32
 #define FP8B_BLOCK_MMA32 1  // block GEMM K step on 32 x 32 x 16 MFMAs (0: 16 x 16 x 32)
 #endif
@@ -1485,7 +1502,7 @@ static void launch_block_any(const uint8_t* a, int64_t lda, const float* sa, con
         launch_decode<4, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
     }
   } else if (M <= 128)
-    launch_block<SmallMCfg, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+    launch_block<SmallMCfg, PK, FP8B_SMALL_MMA32 != 0>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
   else
     launch_block<BlockCfg, PK, FP8B_BLOCK_MMA32 != 0>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
 }
