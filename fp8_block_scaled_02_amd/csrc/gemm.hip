@@ -56,6 +56,9 @@
 namespace fp8blk {
 
 
+#ifndef FP8B_GROUPED_MMA32
+#define FP8B_GROUPED_MMA32 1  // the grouped GEMM's tile items on the 32 x 32 x 16 K step
+#endif
 constexpr int kBK = 128;
 constexpr int kGroupM = 8;  // m-tiles per tile-order group
 
@@ -1305,10 +1308,16 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
         src.soff = (uint32_t)(min(lane, (C::BN + 127) / 128 - 1) * nkb * 4);
         src.scale_dst = C::OFF_SB;
       }
-      v4f acc[C::MI][C::NJ];
-      k_loop<C, PK>(lds0, lds1, lds2, src, nkb, acc);
-      epilogue<C, BF16>(Y, acc, n0,
-                        [&](int r) -> int64_t { return r0 + r < re ? (int64_t)(r0 + r) * N : -1; });
+      auto row_off = [&](int r) -> int64_t { return r0 + r < re ? (int64_t)(r0 + r) * N : -1; };
+      if constexpr (FP8B_GROUPED_MMA32 != 0) {
+        Acc32<C> acc;
+        k_loop32<C, PK>(lds0, lds1, src, nkb, acc);
+        epilogue32<C, BF16>(Y, acc, n0, row_off);
+      } else {
+        v4f acc[C::MI][C::NJ];
+        k_loop<C, PK>(lds0, lds1, lds2, src, nkb, acc);
+        epilogue<C, BF16>(Y, acc, n0, row_off);
+      }
     } else {
       const int sb = wk - n_tile;  // stream item index
       const int e = expert_of(sstart, sb);
