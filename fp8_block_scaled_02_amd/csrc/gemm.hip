@@ -1374,9 +1374,8 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
 #ifndef FP8B_BLOCK_STAGES
 #define FP8B_BLOCK_STAGES 2
 #endif
-// The 64 x 128 small-M tiles stay on the 16 x 16 K step: on the 32 x 32 step
-// (2 x 1 blocks per 64 x 32 wave) 8192 -> 28672 measured 68.4 / 64.9 us
-// against 73.2 / 71.8 at M = 100 / 65, but 79.1 against 77.2 at M = 128.
+// The 64 x 128 tiles keep the 16 x 16 K step (on the 32 x 32 step, 2 x 1
+// blocks per 64 x 32 wave, they measured 2.4% slower at M 128).
 #ifndef FP8B_SMALL_MMA32
 #define FP8B_SMALL_MMA32 0
 #endif
@@ -1390,13 +1389,13 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
 #define FP8B_MX_STAGES 2
 #endif
 using BlockCfg = Cfg<FP8B_BLOCK_CFG, false, FP8B_BLOCK_STAGES>;
-// M up to 128 past the streaming kernel: 64 x 128 tiles (4 waves of
-// 64 x 32), twice the tiles of 128 x 128 so a decode-sized layer fills the
-// chip (measured at 8192 -> 28672: M 64 93 -> 72 us, M 128 95 -> 89 us;
-// three stages were slower).  128 x 64 tiles, which hold every token row
-// of M = 128 in one tile, measured slower (85.7 against 78.6 us at M 128):
-// the two m-tiles of a 64 x 128 column meet in one XCD's L2, so the weights
-// are not streamed twice from HBM.
+// 33 .. 64 tokens on row-major weights (packed weights stream up to 64):
+// 64 x 128 tiles (4 waves of 64 x 32), twice the tiles of 128 x 128.  From
+// 65 tokens on the 128 x 128 tiles of the prefill GEMM (32 x 32 K step)
+// are faster: at 8192 -> 28672, M 128 / 100 took 69.0 / 66.0 us on them
+// against 77.7 / 73.1 on 64 x 128 tiles, whose 448 workgroups leave 192 of
+// the 256 CUs with two to run while each 128 x 128 tile has a CU to itself.
+// (128 x 64 tiles, every token row in one tile, measured 85.7 us at M 128.)
 #ifndef FP8B_SMALL_CFG
 #define FP8B_SMALL_CFG 64, 128, 1, 4, false, 2
 #endif
@@ -1510,7 +1509,7 @@ static void launch_block_any(const uint8_t* a, int64_t lda, const float* sa, con
       else
         launch_decode<4, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
     }
-  } else if (M <= 128)
+  } else if (M <= 64)  // 33 .. 64 tokens on row-major weights
     launch_block<SmallMCfg, PK, FP8B_SMALL_MMA32 != 0>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
   else
     launch_block<BlockCfg, PK, FP8B_BLOCK_MMA32 != 0>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);

@@ -69,7 +69,8 @@ def test_block_gemm_few_tokens(F, orc, M, N, K):
     """M <= 64 takes the streaming decode kernel: one to four 16-token
     subtiles (2- and 1-deep register rings), K-block counts below, at and
     past the prefetch depth and not a multiple of the K split; M = 65 is the
-    first size on 64 x 128 tiles."""
+    first size on 128 x 128 tiles (and 33 .. 64 take 64 x 128 tiles on
+    row-major weights)."""
     c = W.decode_linear(K=K, N=N, seed=M + K)
     yg, yr, bnd = _linear_case(F, orc, c.x[:M], c.w, "ue8m0", torch.bfloat16)
     assert_parity(yg, yr, bnd, True, f"{M}x{N}x{K}")
@@ -152,7 +153,7 @@ def test_linear_step_graph_replay_matches_eager(F, M):
 
 def test_block_gemm_decode_full(F, orc):
     """8192 -> 28672 at every decode size and across the path switches
-    (streaming up to 64 tokens, 64 x 128 tiles up to 128), both weight
+    (streaming up to 64 tokens, then 128 x 128 tiles), both weight
     layouts; sampled token rows x every output column."""
     c = W.decode_linear(device=DEV)
     a, sa = F.fp8_act_quant(c.x, 128, "ue8m0")

@@ -73,8 +73,9 @@ def _quant(F, c, fmt):
 @pytest.mark.parametrize("N,K", [(384, 640), (256, 1152)])
 def test_block_gemm_packed_is_bit_identical(F, M, N, K):
     """Every kernel the block GEMM picks by M (streaming for M <= 16 and
-    <= 32, 64 x 128 tiles to 128, 128 x 128 tiles beyond) with ragged K
-    block counts, both output types."""
+    <= 32, then streaming on packed against 64 x 128 tiles on row-major
+    weights up to 64, 128 x 128 tiles beyond) with ragged K block counts,
+    both output types."""
     c = W.prefill_linear(M=M, N=N, K=K, seed=7 * M + N)
     a, sa, wq, ws = _quant(F, c, "fp32")
     wp = F.fp8_weight_pack(wq)
