@@ -63,12 +63,15 @@ constexpr int kBK = 128;
 constexpr int kGroupM = 8;  // m-tiles per tile-order group
 
 // Tile configuration: BM x BN output tile, WM x WN waves (each TM x TN),
-// S LDS stages (prefetch distance S-1 K steps).
-template <int BM_, int BN_, int WM_, int WN_, bool MX_, int S_>
+// S LDS stages (prefetch distance S-1 K steps), KS groups of WM x WN waves
+// that split the K blocks of a tile between them (group g takes blocks g,
+// g + KS, ...; each group has its own stages, and the groups' partial
+// tiles are summed in LDS at the end).
+template <int BM_, int BN_, int WM_, int WN_, bool MX_, int S_, int KS_ = 1>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_, KS = KS_;
   static constexpr bool MX = MX_;
-  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int NW = WM * WN, NT = 64 * NW * KS;
   static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
   static constexpr int MI = TM / 16, NJ = TN / 16;  // 16x16 subtiles per wave
   static constexpr int MI32 = TM / 32, NJ32 = TN / 32;  // 32x32 blocks per wave (32 x 32 K step)
@@ -90,7 +93,8 @@ struct Cfg {
   static_assert(BN % 128 == 0 || 128 % BN == 0, "a tile's weight rows span whole 128-row scale blocks or lie in one");
   static_assert(TN <= 128, "a wave's columns lie in one weight-scale block");
   static_assert(S == 2 || S == 3, "two or three LDS stages");
-  static_assert(S * BUF <= 160 * 1024, "LDS capacity");
+  static_assert(KS == 1 || (KS == 2 && !MX && S == 2), "K split: two groups, block GEMM, two stages");
+  static_assert(S * BUF * KS <= 160 * 1024, "LDS capacity");
 };
 
 // LDS byte offset of logical 16-byte chunk `ch` (0..7) of tile row `r` (the
@@ -127,13 +131,14 @@ __device__ __forceinline__ void wait_vmem() {
 // The wave index as a scalar (it is uniform; saying so keeps LDS bases and
 // M0 setup in SALU).
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+// The wave's index inside its K group (0 .. NW-1).
+template <class C>
+__device__ __forceinline__ int wave_of() { return wave_id() % C::NW; }
 
-// Map a linear workgroup id to an output tile (tm, tn): first give each XCD
-// a contiguous range of ids (workgroups are dealt to the 8 XCDs round
-// robin), then walk tiles in groups of kGroupM m-tiles so that concurrently
-// running workgroups share A rows and W rows in that XCD's L2.
-__device__ __forceinline__ void tile_of(int pid, int nwg, int tiles_m, int tiles_n, int& tm, int& tn) {
-  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+// Tile pid of a tiles_m x tiles_n grid in groups of kGroupM m-tiles (m
+// fastest inside a group, then n), so that concurrently running ids share
+// A rows and W rows in L2.
+__device__ __forceinline__ void grouped_order(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int per_group = kGroupM * tiles_n;
   const int group = pid / per_group;
   const int first_m = group * kGroupM;
@@ -141,6 +146,14 @@ __device__ __forceinline__ void tile_of(int pid, int nwg, int tiles_m, int tiles
   const int in = pid - group * per_group;
   tm = first_m + in % gsz;
   tn = in / gsz;
+}
+
+// Map a linear workgroup id to an output tile (tm, tn): first give each XCD
+// a contiguous range of ids (workgroups are dealt to the 8 XCDs round
+// robin), then take the grouped order.
+__device__ __forceinline__ void tile_of(int pid, int nwg, int tiles_m, int tiles_n, int& tm, int& tn) {
+  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  grouped_order(pid, tiles_m, tiles_n, tm, tn);
 }
 
 // Per-lane sources of one output tile's direct-to-LDS loads: a uniform base
@@ -166,7 +179,7 @@ struct Src {
 // W group qw from wbase (row_major_woff or packed_woff).
 template <class C, class ARow, class WOff>
 __device__ __forceinline__ void make_code_src(Src<C>& s, ARow arow_off, WOff woff) {
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int lane = threadIdx.x & 63, wave = wave_of<C>();
   const uint32_t chunk = (uint32_t)((lane & 7) ^ (lane >> 3));
 #pragma unroll
   for (int i = 0; i < C::NI; ++i) {
@@ -205,9 +218,12 @@ __device__ __forceinline__ uint32_t packed_woff(int qw, int lane, int np, int nb
   return ((uint32_t)(h * np + pp) << 10) + (uint32_t)(16 * lane);
 }
 
+// Loads the group's kb-th K block (block KS * kb of the bases, which the
+// kernel offsets to the group's first block).
 template <class C>
 __device__ __forceinline__ void issue(uint8_t* buf, const Src<C>& s, int kb) {
-  const int wave = wave_id();
+  const int wave = wave_of<C>();
+  kb *= C::KS;
   const __amdgpu_buffer_rsrc_t ra = rsrc_at(s.abase + (size_t)kb * kBK);
   const __amdgpu_buffer_rsrc_t rw = rsrc_at(s.wbase + (size_t)kb * s.wstep);
 #pragma unroll
@@ -296,7 +312,7 @@ __device__ __forceinline__ Frag16 widen(const Raw16& v, float s_lo, float s_hi) 
 template <class C, bool PK, class Hook>
 __device__ __forceinline__ void compute_block(const uint8_t* buf, v4f (&acc)[C::MI][C::NJ], Hook hook) {
   static_assert(C::MI == 4, "one rescale row per K sub-step window");
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int lane = threadIdx.x & 63, wave = wave_of<C>();
   const int wm = wave % C::WM, wn = wave / C::WM, l16 = lane & 15, g = lane >> 4;
   const float* sa = reinterpret_cast<const float*>(buf + C::OFF_SA);
   const float* sw = reinterpret_cast<const float*>(buf + C::OFF_SB);
@@ -393,7 +409,7 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
 // (K 64+16g..) in 32-block 2 + g/2; scale bytes are one dword per row.
 template <class C, class Hook>
 __device__ __forceinline__ void compute_mx(const uint8_t* buf, v4f (&acc)[C::MI][C::NJ], Hook hook) {
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int lane = threadIdx.x & 63, wave = wave_of<C>();
   const int wm = wave % C::WM, wn = wave / C::WM, l16 = lane & 15, g = lane >> 4;
   const uint32_t* ea = reinterpret_cast<const uint32_t*>(buf + C::OFF_SA);
   const uint32_t* eb = reinterpret_cast<const uint32_t*>(buf + C::OFF_SB);
@@ -517,7 +533,7 @@ __device__ __forceinline__ void store4(void* __restrict__ y, int64_t off, const 
 template <class C, bool BF16, class RowOff>
 __device__ __forceinline__ void epilogue(void* __restrict__ y, const v4f (&acc)[C::MI][C::NJ], int n0,
                                          RowOff row_off) {
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int lane = threadIdx.x & 63, wave = wave_of<C>();
   const int wm = wave % C::WM, wn = wave / C::WM, l16 = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int i = 0; i < C::MI; ++i) {
@@ -587,7 +603,7 @@ __device__ __forceinline__ void compute_block32(const uint8_t* buf, Acc32<C>& ac
                                                 const float (&sp)[C::MI32], float (&sn)[C::MI32], Hook hook) {
   constexpr int MI = C::MI32, NJ = C::NJ32;
   static_assert(C::TM == 32 * MI && C::TN == 32 * NJ && MI <= 2 && NJ <= 2, "32 x 32 blocks per wave");
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int lane = threadIdx.x & 63, wave = wave_of<C>();
   const int wm = wave % C::WM, wn = wave / C::WM, r = lane & 31, h = lane >> 5;
   const float* sa = reinterpret_cast<const float*>(buf + C::OFF_SA);
   const float* sw = reinterpret_cast<const float*>(buf + C::OFF_SB);
@@ -698,7 +714,7 @@ __device__ __forceinline__ void k_loop32(uint8_t* l0, uint8_t* l1, const Src<C>&
 
 template <class C, bool BF16, class RowOff>
 __device__ __forceinline__ void epilogue32(void* __restrict__ y, const Acc32<C>& acc, int n0, RowOff row_off) {
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int lane = threadIdx.x & 63, wave = wave_of<C>();
   const int wm = wave % C::WM, wn = wave / C::WM, r = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int i = 0; i < C::MI32; ++i) {
@@ -717,57 +733,101 @@ __device__ __forceinline__ void epilogue32(void* __restrict__ y, const Acc32<C>&
 // Stage arrays: a kernel declares all three (unused ones cost nothing; the
 // compiler drops them) so one body serves S = 2 and S = 3.
 #define FP8B_STAGES(C)                                                          \
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[C::BUF];                 \
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[C::BUF];                 \
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[C::BUF * C::KS];         \
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[C::BUF * C::KS];         \
   __shared__ __attribute__((aligned(16))) uint8_t lds2[C::S == 3 ? C::BUF : 16]
 
 // ---- block-scaled GEMM ------------------------------------------------------
 // Occupancy: 512-thread tiles run one workgroup per CU (2 waves per SIMD);
 // 256-thread tiles two.
+//
+// With a K split (C::KS = 2, for grids that leave CUs without a second
+// tile), the two 4-wave groups of a workgroup run the same K loop over
+// alternate K blocks, each on its own two stages: both groups take the same
+// number of blocks, so their barriers pair up.  At the end group 1 leaves
+// its partial tile in LDS and group 0 adds it (fp32) before the epilogue.
+template <class C>
+__device__ __forceinline__ void ksplit_sum(uint8_t* lds, Acc32<C>& acc) {
+  static_assert(C::KS == 2 && C::NW * C::MI32 * C::NJ32 * 4 * 1024 <= C::BUF * C::KS, "partials fit in LDS");
+  const int lane = threadIdx.x & 63, wave = wave_of<C>(), group = wave_id() / C::NW;
+  v4f* x = reinterpret_cast<v4f*>(lds) + wave * (C::MI32 * C::NJ32 * 4 * 64) + lane;
+  __syncthreads();  // both groups are done with the stages
+  if (group == 1) {
+#pragma unroll
+    for (int i = 0; i < C::MI32; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NJ32; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          x[((i * C::NJ32 + j) * 4 + q) * 64] =
+              v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+  }
+  __syncthreads();
+  if (group == 0) {
+#pragma unroll
+    for (int i = 0; i < C::MI32; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NJ32; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v4f o = x[((i * C::NJ32 + j) * 4 + q) * 64];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[i][j][4 * q + v] += o[v];
+        }
+  }
+}
+
 template <class C, bool BF16, bool PK, bool M32 = false>
 __global__ __launch_bounds__(C::NT, 512 / C::NT) void block_gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ SA,
     const uint8_t* __restrict__ W, int64_t ldw, const float* __restrict__ SW, int M, int N, int K,
     void* __restrict__ Y, int64_t ldy) {
+  static_assert(C::KS == 1 || M32, "the K split runs on the 32 x 32 K step");
   FP8B_STAGES(C);
   const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = N / C::BN;
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * C::BM, n0 = tn * C::BN, nkb = K / kBK;
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int lane = threadIdx.x & 63, wave = wave_of<C>();
+  const int group = C::KS > 1 ? wave_id() / C::NW : 0;  // this group's first K block
+  const int nkb = K / kBK, nkb_g = nkb / C::KS;          // the launcher keeps nkb % KS == 0
 
   Src<C> src;
   // 64-bit tile bases, 32-bit per-lane offsets inside the tile (the entry
   // point keeps every leading dimension below 2^24); rows past M re-read
   // the last row and their results are never stored
   const int mlast = M - 1 - m0;
-  src.abase = A + (int64_t)m0 * lda;
+  src.abase = A + (int64_t)m0 * lda + group * kBK;
   if (PK) {
-    src.wbase = W + (int64_t)(n0 / 16) * 1024;
+    src.wbase = W + (int64_t)(n0 / 16) * 1024 + (int64_t)group * N * kBK;
     src.wstep = (size_t)N * kBK;
     make_code_src<C>(src, [&](int r) { return (uint32_t)(min(r, mlast) * lda); },
                      [&](int qw, int l) { return packed_woff(qw, l, N / 16, C::BN / 16); });
   } else {
-    src.wbase = W + (int64_t)n0 * ldw;
+    src.wbase = W + (int64_t)n0 * ldw + group * kBK;
     src.wstep = kBK;
     make_code_src<C>(src, [&](int r) { return (uint32_t)(min(r, mlast) * lda); },
                      [&](int qw, int l) { return row_major_woff(qw, l, ldw); });
   }
   src.scale_dst = -1;
-  src.sbase = reinterpret_cast<const uint8_t*>(SA + (int64_t)m0 * nkb);
+  src.sbase = reinterpret_cast<const uint8_t*>(SA + (int64_t)m0 * nkb + group);
   src.soff = 0;
   if (wave < C::NS_A) {
     src.soff = (uint32_t)(min(64 * wave + lane, mlast) * nkb * 4);
     src.scale_dst = C::OFF_SA + 256 * wave;
   } else if (wave == C::NS_A) {
-    src.sbase = reinterpret_cast<const uint8_t*>(SW + (int64_t)(n0 / 128) * nkb);
+    src.sbase = reinterpret_cast<const uint8_t*>(SW + (int64_t)(n0 / 128) * nkb + group);
     src.soff = (uint32_t)(min(lane, (C::BN + 127) / 128 - 1) * nkb * 4);
     src.scale_dst = C::OFF_SB;
   }
 
   if constexpr (M32) {
     Acc32<C> acc;
-    k_loop32<C, PK>(lds0, lds1, src, nkb, acc);
+    k_loop32<C, PK>(lds0 + group * C::BUF, lds1 + group * C::BUF, src, nkb_g, acc);
+    if constexpr (C::KS > 1) {
+      ksplit_sum<C>(lds0, acc);
+      if (group != 0) return;
+    }
     epilogue32<C, BF16>(Y, acc, n0, [&](int r) -> int64_t { return m0 + r < M ? (int64_t)(m0 + r) * ldy : -1; });
   } else {
     v4f acc[C::MI][C::NJ];
@@ -839,7 +899,7 @@ __device__ __forceinline__ void mx_exact_tile(const uint8_t* __restrict__ A, int
                                            int M, int K, int m0, int n0, float* __restrict__ Y, int64_t ldy) {
   constexpr int JG = 2;
   static_assert(C::NJ % JG == 0, "weight subtiles per pass");
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int lane = threadIdx.x & 63, wave = wave_of<C>();
   const int wm = wave % C::WM, wn = wave / C::WM, l16 = lane & 15, g = lane >> 4;
   const int srow = K / 32, nkb = K / kBK;
   const uint8_t* arow[C::MI];
@@ -921,7 +981,7 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void mx_gemm_kernel(
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN, nkb = K / kBK;
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int lane = threadIdx.x & 63, wave = wave_of<C>();
   const int srow = K / 32;  // E8M0 bytes per row
 
   Src<C> src;
@@ -1184,20 +1244,27 @@ __global__ __launch_bounds__(256) void decode_gemm_kernel(
 // Persistent workgroups over two kinds of work item, both mapped in LDS by
 // every workgroup from expert_offsets (prefix sums of per-expert counts), so
 // the host never reads the routing:
-//  * tile items: 128 x 128 output tiles of an expert's rows, ordered
-//    (expert, n-tile, m-tile) with m fastest, so concurrently running m-tiles
-//    of a heavy expert share its weight tile in L2;
+//  * tile items: 128 x 128 output tiles of an expert's rows, per expert in
+//    the grouped order of the block GEMM (kGroupM m-tiles at a time, m
+//    fastest), so concurrently running tiles of a heavy expert share weight
+//    tiles and token rows in L2;
 //  * stream items: an expert's last (rows mod 128) rows when there are at
 //    most kStreamTail of them (most experts of a skewed routing have only a
 //    few rows): 64 weight rows each, on the streaming path, so a 5-row
 //    expert costs one pass over its weights instead of 128-row tiles of MFMA
 //    work.
-// Tile items come first and the fine-grained stream items fill the end of the
-// run (measured on MI355X with a Zipf-skewed 256-expert routing: 3-6% faster
-// than interleaving the two kinds evenly or putting stream items first).
-// Each XCD gets a contiguous run of work ids per round (workgroups are dealt
-// to the 8 XCDs round robin), so consecutive m-tiles of one weight tile meet
-// in one L2 (7-15% faster than the plain order).
+// Tile items are bound by MFMA issue and stream items by HBM, so the two
+// workgroups that share a CU should run different kinds at the same time.
+// The grid is two halves of equal shares: half 0 takes the first half of
+// the tile items and of the stream items, half 1 the rest; half 0 runs its
+// tile items first and half 1 its stream items first.  The dispatcher fills
+// the CUs breadth-first (measured on MI355X: with 2 x 256 workgroups of this
+// kernel's size, workgroups b and b + 256 share a CU, b in its first wave
+// slots), so each CU pairs a tile-first and a stream-first workgroup; if it
+// did not, only the speed would change.  Within a half, each XCD gets a
+// contiguous run of work ids per round (workgroups are dealt to the 8 XCDs
+// round robin), so consecutive m-tiles of one weight tile meet in one L2
+// (7-15% faster than the plain order).
 constexpr int kMaxExperts = 1024;
 constexpr int kStreamTail = 32;
 
@@ -1213,7 +1280,7 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
   __shared__ int tstart[kMaxExperts + 1];  // first tile item of expert e
   __shared__ int sstart[kMaxExperts + 1];  // first stream item of expert e
   __shared__ int scan[2][C::NT];
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_of<C>();
   const int tiles_n = N / C::BN, nkb = K / kBK, sblocks = N / kStreamRows;
 
   auto off_at = [&](int e) { return min(max(OFFS[e], 0), R); };
@@ -1257,7 +1324,6 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
   }
   __syncthreads();
   const int n_tile = tstart[E], n_stream = sstart[E];
-  const int total = n_tile + n_stream;
   // largest e with start[e] <= w
   auto expert_of = [&](const int* start, int w) {
     int lo = 0, hi = E;
@@ -1268,95 +1334,113 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
     return lo;
   };
 
+  // the two halves (a grid that is not a multiple of 16 runs as one half)
   const int G = gridDim.x;
-  const int slot = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-  for (int base = 0; base < total; base += G) {
-    const int wk = base + slot;
-    if (wk >= total) break;
-    __syncthreads();  // the previous item may still read the stages / partials
+  const bool two = G >= 16 && (G & 15) == 0;
+  const int Gh = two ? G >> 1 : G;
+  const int half = two && (int)blockIdx.x >= Gh ? 1 : 0;
+  const int bl = (int)blockIdx.x - half * Gh;
+  const int slot = (Gh & 7) == 0 ? (bl & 7) * (Gh >> 3) + (bl >> 3) : bl;
+  // Shares balanced on measured co-running costs (a stream item beside a
+  // tile item takes 7/16 of a tile item's time): half 1 runs the stream
+  // items [0, ns1) and then the last x1 tile items, half 0 the other tile
+  // items and then the stream items [ns1, n_stream).
+  int x1 = 0, ns1 = n_stream;
+  if (!two) ns1 = 0;
+  else if (16 * n_tile >= 7 * n_stream) x1 = (16 * n_tile - 7 * n_stream) / 32;
+  else ns1 = n_stream - (7 * n_stream - 16 * n_tile) / 14;
+  const int nt0 = n_tile - x1;
+  for (int phase = 0; phase < 2; ++phase) {
+    const bool tiles = (phase == 0) == (half == 0);
+    const int first = tiles ? (half == 0 ? 0 : nt0) : (half == 0 ? ns1 : 0);
+    const int end = tiles ? (half == 0 ? nt0 : n_tile) : (half == 0 ? n_stream : ns1);
+    for (int item = first + slot; item < end; item += Gh) {
+      __syncthreads();  // the previous item may still read the stages / partials
 
-    if (wk < n_tile) {
-      const int e = expert_of(tstart, wk);
-      const int rb = off_at(e), re = rb + rows_of(e) - tail_of(e);
-      const int mt = (re - rb + C::BM - 1) / C::BM;
-      const int loc = wk - tstart[e];
-      const int tn = loc / mt, tm = loc - tn * mt;
-      const int r0 = rb + tm * C::BM, n0 = tn * C::BN;
-      auto token = [&](int r) { return min(max(RI[min(r0 + r, re - 1)], 0), T - 1); };
+      if (tiles) {
+        const int wk = item;  // tile item index
+        const int e = expert_of(tstart, wk);
+        const int rb = off_at(e), re = rb + rows_of(e) - tail_of(e);
+        const int mt = (re - rb + C::BM - 1) / C::BM;
+        int tm, tn;
+        grouped_order(wk - tstart[e], mt, tiles_n, tm, tn);
+        const int r0 = rb + tm * C::BM, n0 = tn * C::BN;
+        auto token = [&](int r) { return min(max(RI[min(r0 + r, re - 1)], 0), T - 1); };
 
-      Src<C> src;
-      src.abase = A;
-      if (PK) {
-        src.wbase = W + (int64_t)e * N * K + (int64_t)(n0 / 16) * 1024;
-        src.wstep = (size_t)N * kBK;
-        make_code_src<C>(src, [&](int r) { return (uint32_t)token(r) * (uint32_t)K; },
-                         [&](int qw, int l) { return packed_woff(qw, l, N / 16, C::BN / 16); });
-      } else {
-        src.wbase = W + ((int64_t)e * N + n0) * K;
-        src.wstep = kBK;
-        make_code_src<C>(src, [&](int r) { return (uint32_t)token(r) * (uint32_t)K; },
-                         [&](int qw, int l) { return row_major_woff(qw, l, K); });
-      }
-      src.scale_dst = -1;
-      src.sbase = reinterpret_cast<const uint8_t*>(SA);
-      src.soff = 0;
-      if (wave < C::NS_A) {
-        src.soff = (uint32_t)token(64 * wave + lane) * (uint32_t)(nkb * 4);
-        src.scale_dst = C::OFF_SA + 256 * wave;
-      } else if (wave == C::NS_A) {
-        src.sbase = reinterpret_cast<const uint8_t*>(SW + ((int64_t)e * (N / 128) + n0 / 128) * nkb);
-        src.soff = (uint32_t)(min(lane, (C::BN + 127) / 128 - 1) * nkb * 4);
-        src.scale_dst = C::OFF_SB;
-      }
-      auto row_off = [&](int r) -> int64_t { return r0 + r < re ? (int64_t)(r0 + r) * N : -1; };
-      if constexpr (FP8B_GROUPED_MMA32 != 0) {
-        Acc32<C> acc;
-        k_loop32<C, PK>(lds0, lds1, src, nkb, acc);
-        epilogue32<C, BF16>(Y, acc, n0, row_off);
-      } else {
-        v4f acc[C::MI][C::NJ];
-        k_loop<C, PK>(lds0, lds1, lds2, src, nkb, acc);
-        epilogue<C, BF16>(Y, acc, n0, row_off);
-      }
-    } else {
-      const int sb = wk - n_tile;  // stream item index
-      const int e = expert_of(sstart, sb);
-      const int t = tail_of(e), r0 = off_at(e) + rows_of(e) - t;
-      const int n0 = (sb - sstart[e]) * kStreamRows;
-      const int l16 = lane & 15;
-      const uint8_t* wrow = PK ? W + (int64_t)e * N * K + (int64_t)(n0 / 16) * 1024 + 16 * lane
-                               : W + ((int64_t)e * N + n0 + l16) * K;
-      const int64_t cs = (int64_t)(N / 16) * 1024;
-      const float* swrow = SW + ((int64_t)e * (N / 128) + n0 / 128) * nkb;
-      v4f* part = reinterpret_cast<v4f*>(lds0);
-      auto row_off = [&](int r) -> int64_t { return r < t ? (int64_t)(r0 + r) * N : -1; };
-      auto run = [&](auto mi) {
-        constexpr int MI = decltype(mi)::value;
-        auto token = [&](int r) { return min(max(RI[r0 + min(r, t - 1)], 0), T - 1); };
-        const uint8_t* aline[MI][2];
-        const float* sarow[MI];
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          sarow[i] = SA + (int64_t)token(16 * i + l16) * nkb;
-#pragma unroll
-          for (int q = 0; q < 2; ++q)
-            aline[i][q] = A + (int64_t)token(16 * i + 8 * q + (lane >> 3)) * K + 16 * (lane & 7);
+        Src<C> src;
+        src.abase = A;
+        if (PK) {
+          src.wbase = W + (int64_t)e * N * K + (int64_t)(n0 / 16) * 1024;
+          src.wstep = (size_t)N * kBK;
+          make_code_src<C>(src, [&](int r) { return (uint32_t)token(r) * (uint32_t)K; },
+                           [&](int qw, int l) { return packed_woff(qw, l, N / 16, C::BN / 16); });
+        } else {
+          src.wbase = W + ((int64_t)e * N + n0) * K;
+          src.wstep = kBK;
+          make_code_src<C>(src, [&](int r) { return (uint32_t)token(r) * (uint32_t)K; },
+                           [&](int qw, int l) { return row_major_woff(qw, l, K); });
         }
-        v4f acc[MI][kStreamNJ];
-        bool mine;
-        if (PK)
-          mine = stream_rows<MI>(aline, sarow, [&](int j, int kb) { return load_frag_packed(wrow, cs, j, kb); },
-                                 swrow, nkb, lds1, part, acc);
+        src.scale_dst = -1;
+        src.sbase = reinterpret_cast<const uint8_t*>(SA);
+        src.soff = 0;
+        if (wave < C::NS_A) {
+          src.soff = (uint32_t)token(64 * wave + lane) * (uint32_t)(nkb * 4);
+          src.scale_dst = C::OFF_SA + 256 * wave;
+        } else if (wave == C::NS_A) {
+          src.sbase = reinterpret_cast<const uint8_t*>(SW + ((int64_t)e * (N / 128) + n0 / 128) * nkb);
+          src.soff = (uint32_t)(min(lane, (C::BN + 127) / 128 - 1) * nkb * 4);
+          src.scale_dst = C::OFF_SB;
+        }
+        auto row_off = [&](int r) -> int64_t { return r0 + r < re ? (int64_t)(r0 + r) * N : -1; };
+        if constexpr (FP8B_GROUPED_MMA32 != 0) {
+          Acc32<C> acc;
+          k_loop32<C, PK>(lds0, lds1, src, nkb, acc);
+          epilogue32<C, BF16>(Y, acc, n0, row_off);
+        } else {
+          v4f acc[C::MI][C::NJ];
+          k_loop<C, PK>(lds0, lds1, lds2, src, nkb, acc);
+          epilogue<C, BF16>(Y, acc, n0, row_off);
+        }
+      } else {
+        const int sb = item;  // stream item index
+        const int e = expert_of(sstart, sb);
+        const int t = tail_of(e), r0 = off_at(e) + rows_of(e) - t;
+        const int n0 = (sb - sstart[e]) * kStreamRows;
+        const int l16 = lane & 15;
+        const uint8_t* wrow = PK ? W + (int64_t)e * N * K + (int64_t)(n0 / 16) * 1024 + 16 * lane
+                                 : W + ((int64_t)e * N + n0 + l16) * K;
+        const int64_t cs = (int64_t)(N / 16) * 1024;
+        const float* swrow = SW + ((int64_t)e * (N / 128) + n0 / 128) * nkb;
+        v4f* part = reinterpret_cast<v4f*>(lds0);
+        auto row_off = [&](int r) -> int64_t { return r < t ? (int64_t)(r0 + r) * N : -1; };
+        auto run = [&](auto mi) {
+          constexpr int MI = decltype(mi)::value;
+          auto token = [&](int r) { return min(max(RI[r0 + min(r, t - 1)], 0), T - 1); };
+          const uint8_t* aline[MI][2];
+          const float* sarow[MI];
+  #pragma unroll
+          for (int i = 0; i < MI; ++i) {
+            sarow[i] = SA + (int64_t)token(16 * i + l16) * nkb;
+  #pragma unroll
+            for (int q = 0; q < 2; ++q)
+              aline[i][q] = A + (int64_t)token(16 * i + 8 * q + (lane >> 3)) * K + 16 * (lane & 7);
+          }
+          v4f acc[MI][kStreamNJ];
+          bool mine;
+          if (PK)
+            mine = stream_rows<MI>(aline, sarow, [&](int j, int kb) { return load_frag_packed(wrow, cs, j, kb); },
+                                   swrow, nkb, lds1, part, acc);
+          else
+            mine = stream_rows<MI>(aline, sarow, [&](int j, int kb) {
+              return load_frag_global(wrow + (int64_t)16 * j * K + (int64_t)kb * kBK);
+            }, swrow, nkb, lds1, part, acc);
+          if (mine) stream_store<MI, BF16>(Y, acc, n0, row_off);
+        };
+        if (t <= 16)
+          run(std::integral_constant<int, 1>{});
         else
-          mine = stream_rows<MI>(aline, sarow, [&](int j, int kb) {
-            return load_frag_global(wrow + (int64_t)16 * j * K + (int64_t)kb * kBK);
-          }, swrow, nkb, lds1, part, acc);
-        if (mine) stream_store<MI, BF16>(Y, acc, n0, row_off);
-      };
-      if (t <= 16)
-        run(std::integral_constant<int, 1>{});
-      else
-        run(std::integral_constant<int, 2>{});
+          run(std::integral_constant<int, 2>{});
+      }
     }
   }
 }
@@ -1389,6 +1473,13 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
 #define FP8B_MX_STAGES 2
 #endif
 using BlockCfg = Cfg<FP8B_BLOCK_CFG, false, FP8B_BLOCK_STAGES>;
+// Grids of at most one 128 x 128 tile per CU (65 .. 128 tokens at decode
+// widths) leave each tile's CU one 4-wave workgroup, one wave per SIMD; the
+// K-split form gives it both halves of the K range on two 4-wave groups.
+#ifndef FP8B_BLOCK_KSPLIT
+#define FP8B_BLOCK_KSPLIT 1
+#endif
+using BlockKsCfg = Cfg<FP8B_BLOCK_CFG, false, 2, 2>;
 // 33 .. 64 tokens on row-major weights (packed weights stream up to 64):
 // 64 x 128 tiles (4 waves of 64 x 32), twice the tiles of 128 x 128.  From
 // 65 tokens on the 128 x 128 tiles of the prefill GEMM (32 x 32 K step)
@@ -1509,10 +1600,15 @@ static void launch_block_any(const uint8_t* a, int64_t lda, const float* sa, con
       else
         launch_decode<4, PK>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
     }
-  } else if (M <= 64)  // 33 .. 64 tokens on row-major weights
+  } else if (M <= 64) {  // 33 .. 64 tokens on row-major weights
     launch_block<SmallMCfg, PK, FP8B_SMALL_MMA32 != 0>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
-  else
-    launch_block<BlockCfg, PK, FP8B_BLOCK_MMA32 != 0>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+  } else {
+    const int64_t tiles = ((M + BlockCfg::BM - 1) / BlockCfg::BM) * (N / BlockCfg::BN);
+    if (FP8B_BLOCK_KSPLIT && tiles <= cu_count(s) && (K / kBK) % 2 == 0)
+      launch_block<BlockKsCfg, PK, true>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+    else
+      launch_block<BlockCfg, PK, FP8B_BLOCK_MMA32 != 0>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+  }
 }
 
 int launch_block_gemm(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,

@@ -170,6 +170,28 @@ def test_block_gemm_decode_full(F, orc):
             assert_parity(_np(y[rows]), yr, bnd, True, f"decode M={M} {name}")
 
 
+@pytest.mark.parametrize("M,N,K", [(65, 128, 256), (128, 256, 768), (100, 384, 1024), (256, 512, 2048),
+                                   (128, 256, 384), (97, 40960, 256)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_block_gemm_k_split(F, orc, M, N, K, out):
+    """Grids of at most one 128 x 128 tile per CU with an even K-block count
+    split K between two wave groups (one, three and four blocks per group;
+    two m-tiles); an odd count (K 384) and a grid wider than the CU count
+    (97 x 40960, 320 tiles) keep the unsplit kernel.  Both weight layouts,
+    sampled rows x every column on the wide case."""
+    c = W.prefill_linear(M=M, K=K, N=N, seed=7 * M + K)
+    a, sa = F.fp8_act_quant(c.x.to(DEV), 128, "fp32")
+    wq, ws = F.fp8_weight_quant(c.w.to(DEV), "fp32")
+    rows = list(range(M)) if N * M <= 1 << 17 else sorted({0, 1, M // 2, M - 1})
+    oa, osa = orc.act_quant(W.bits(c.x[rows]), 128, 0)
+    ow, osw = orc.weight_quant(W.bits(c.w), 0)
+    yr, bnd = orc.block_gemm(oa, osa, ow, osw)
+    for name, y in (("row-major", F.fp8_block_gemm(a, sa, wq, ws, out)),
+                    ("packed", F.fp8_block_gemm_packed(a, sa, F.fp8_weight_pack(wq), ws, out))):
+        torch.cuda.synchronize()
+        assert_parity(_np(y[rows]), yr, bnd, out == torch.bfloat16, f"{M}x{N}x{K} {name}")
+
+
 def test_block_gemm_prefill_full_sampled(F, orc):
     c = W.prefill_linear(device=DEV)
     rows = [0, 1, 127, 128, 1000, 2047, 2048, 3071, 4094, 4095]
@@ -330,6 +352,32 @@ def test_grouped_scale_products_near_the_fp32_range_ends(F, orc, scale):
                   F.fp8_grouped_gemm_packed(ta, tsa, tri, tof, F.fp8_weight_pack(tw), tsw, out)):
             torch.cuda.synchronize()
             assert_parity(_np(y), yr, bnd, out == torch.bfloat16, f"grouped, scale products {scale}")
+
+
+@pytest.mark.parametrize("counts", [[200, 150] + [3] * 62,
+                                    [600, 500, 400, 300, 2, 5, 9] + [0] * 57])
+def test_grouped_two_half_schedule(F, orc, counts):
+    """64 experts at N 1024 give a 512-workgroup grid, which splits into a
+    tile-first and a stream-first half: stream items outweighing tile items
+    (the tile-first half also takes stream items) and the reverse (the
+    stream-first half also takes the last tile items); both layouts."""
+    case = _moe_counts_case(counts, T=2048, N=1024, K=256, seed=47)
+    E, N, K = case.w.shape
+    a, sa = F.fp8_act_quant(case.x.to(DEV), 128, "fp32")
+    wq = torch.empty(E, N, K, dtype=torch.uint8, device=DEV)
+    ws = torch.empty(E, N // 128, K // 128, dtype=torch.float32, device=DEV)
+    for e in range(E):
+        F.fp8_weight_quant(case.w[e].to(DEV), "fp32", q=wq[e], scales=ws[e])
+    ri, offs = case.row_index.to(DEV), case.offs.to(DEV)
+    R = case.row_index.shape[0]
+    oa, osa = orc.act_quant(W.bits(case.x), 128, 0)
+    wl, sl = zip(*(orc.weight_quant(W.bits(case.w[e]), 0) for e in range(E)))
+    yr, bnd = orc.grouped_gemm(oa, osa, case.row_index.numpy(), case.offs.numpy(), list(wl), list(sl))
+    for name, y in (("row-major", F.fp8_grouped_gemm(a, sa, ri, offs, wq, ws, torch.bfloat16)),
+                    ("packed", F.fp8_grouped_gemm_packed(a, sa, ri, offs, F.fp8_weight_pack(wq), ws, torch.bfloat16))):
+        torch.cuda.synchronize()
+        assert y.shape == (R, N)
+        assert_parity(_np(y), yr, bnd, True, f"two halves {name}")
 
 
 def test_grouped_only_short_experts(F, orc):
