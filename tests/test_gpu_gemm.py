@@ -192,6 +192,26 @@ def test_block_gemm_k_split(F, orc, M, N, K, out):
         assert_parity(_np(y[rows]), yr, bnd, out == torch.bfloat16, f"{M}x{N}x{K} {name}")
 
 
+@pytest.mark.parametrize("M,N", [(2000, 2304), (2048, 2176)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_block_gemm_grids_wider_than_the_chip(F, orc, M, N, out):
+    """128 x 128 tile grids of more tiles than CUs (288 and 272, so no K
+    split), N a multiple of 256 and not; a ragged last m-tile (M 2000);
+    both weight layouts; sampled rows across m-tiles x every column."""
+    K = 512
+    c = W.prefill_linear(M=M, K=K, N=N, seed=M + N)
+    a, sa = F.fp8_act_quant(c.x.to(DEV), 128, "fp32")
+    wq, ws = F.fp8_weight_quant(c.w.to(DEV), "fp32")
+    rows = [0, 1, 127, 128, 1000, M - 2, M - 1]
+    oa, osa = orc.act_quant(W.bits(c.x[rows]), 128, 0)
+    ow, osw = orc.weight_quant(W.bits(c.w), 0)
+    yr, bnd = orc.block_gemm(oa, osa, ow, osw)
+    for name, y in (("row-major", F.fp8_block_gemm(a, sa, wq, ws, out)),
+                    ("packed", F.fp8_block_gemm_packed(a, sa, F.fp8_weight_pack(wq), ws, out))):
+        torch.cuda.synchronize()
+        assert_parity(_np(y[rows]), yr, bnd, out == torch.bfloat16, f"{M}x{N}x{K} {name}")
+
+
 def test_block_gemm_prefill_full_sampled(F, orc):
     c = W.prefill_linear(device=DEV)
     rows = [0, 1, 127, 128, 1000, 2047, 2048, 3071, 4094, 4095]
