@@ -1341,14 +1341,21 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
   const int half = two && (int)blockIdx.x >= Gh ? 1 : 0;
   const int bl = (int)blockIdx.x - half * Gh;
   const int slot = (Gh & 7) == 0 ? (bl & 7) * (Gh >> 3) + (bl >> 3) : bl;
-  // Shares balanced on measured co-running costs (a stream item beside a
-  // tile item takes 7/16 of a tile item's time): half 1 runs the stream
-  // items [0, ns1) and then the last x1 tile items, half 0 the other tile
-  // items and then the stream items [ns1, n_stream).
+  // Shares balanced on measured co-running costs (per-item timeline of a
+  // 256-expert launch on MI355X): a tile item took 82 us on a half-0
+  // workgroup and 102 us on a half-1 one (the later wave slots lose issue
+  // arbitration to their older partner), a stream item 36 us beside a tile
+  // item.  Half 1 runs the stream items [0, ns1) and then the last x1 tile
+  // items, half 0 the other tile items and then the stream items
+  // [ns1, n_stream): x1 = (82 tiles - 36 streams) / (82 + 102), or, when the
+  // stream items outweigh the tile items, half 0 takes the surplus ones.
+  // (Interleaved on two boxes this share beat 7/16-weighted shares by 1.7
+  // and 2.3%; re-fitting the costs under it gave a smaller x1 that measured
+  // 1.9% slower than this one.)
   int x1 = 0, ns1 = n_stream;
   if (!two) ns1 = 0;
-  else if (16 * n_tile >= 7 * n_stream) x1 = (16 * n_tile - 7 * n_stream) / 32;
-  else ns1 = n_stream - (7 * n_stream - 16 * n_tile) / 14;
+  else if (41 * n_tile >= 18 * n_stream) x1 = (41 * n_tile - 18 * n_stream) / 92;
+  else ns1 = n_stream - (18 * n_stream - 41 * n_tile) / 36;
   const int nt0 = n_tile - x1;
   for (int phase = 0; phase < 2; ++phase) {
     const bool tiles = (phase == 0) == (half == 0);

@@ -84,16 +84,17 @@ def test_block_gemm_ue8m0_small(F, orc):
     assert_parity(yg, yr, bnd, True, "ue8m0 128x512x1024")
 
 
-@pytest.mark.parametrize("M", [1, 40, 100, 300])
+@pytest.mark.parametrize("M,K", [(1, 256), (40, 256), (100, 256), (300, 256), (300, 384)])
 @pytest.mark.parametrize("scale", ["small", "large"])
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
-def test_block_gemm_scale_products_near_the_fp32_range_ends(F, orc, M, scale, out):
+def test_block_gemm_scale_products_near_the_fp32_range_ends(F, orc, M, K, scale, out):
     """Hand-made codes and scales whose per-block products a_scales * w_scales
     lie just above fp32's smallest normal (2^-126 .. 2^-122) or near 2^100,
-    on every path (streaming for M <= 64, 64- and 128-row tiles) and both
-    weight layouts."""
-    rng = np.random.default_rng(31 + M)
-    N, K = 256, 256
+    on every path (streaming for M <= 64 on packed weights, 64-row tiles for
+    M 40 on row-major ones, 128-row tiles with the K split at two K blocks and
+    without it at three) and both weight layouts."""
+    rng = np.random.default_rng(31 + M + K)
+    N = 256
 
     def codes(rows):
         c = rng.integers(0, 0x7F, size=(rows, K)).astype(np.uint8)   # 0x7F is NaN
