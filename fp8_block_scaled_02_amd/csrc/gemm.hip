@@ -1095,14 +1095,33 @@ constexpr int stream_part_bytes() {
 // the lines into its MFMA fragment through a private LDS tile in lds_a,
 // 4 * MI * 2048 bytes per workgroup); sarow[i]: the per-block scales of
 // this lane's row 16i + l16; wload(j, kb): this lane's fragment of weight
-// subtile j at K block kb; swrow: the weight-scale row of these rows.
+// subtile j at K block kb; ws: the weight-scale rows of these rows.
 // Every wave of the workgroup must call it; the sums are complete in wave 0
 // only (the return value says which), and `part` may be reused by the
 // caller only after a barrier.
+// Weight-scale rows of a streaming workgroup's 16 * NJ rows: subtiles
+// j < split take row lo, the others row hi.  A 16-row subtile never
+// straddles a 128-row scale block, but a workgroup of 16 * NJ rows can when
+// 16 * NJ does not divide 128 (112-row workgroups: rows 112 .. 223 take
+// blocks 0 and 1); hi then is the next block's row (clamped to the last, so
+// it is always a valid address).
+struct WScales {
+  const float* lo;
+  const float* hi;
+  int split;
+};
+
+__device__ __forceinline__ WScales wscales_of(const float* sw_rows, int n0, int n_rows, int nkb) {
+  const int b = n0 / 128;
+  return WScales{sw_rows + (int64_t)b * nkb, sw_rows + (int64_t)min(b + 1, n_rows / 128 - 1) * nkb,
+                 (128 - n0 % 128) / 16};
+}
+
 template <int MI, int NJ = kStreamNJ, int D = kStreamDepth, class WLoad>
 __device__ __forceinline__ bool stream_rows(const uint8_t* const (&aline)[MI][2], const float* const (&sarow)[MI],
-                                            WLoad wload, const float* swrow, int nkb, uint8_t* lds_a,
+                                            WLoad wload, const WScales& ws, int nkb, uint8_t* lds_a,
                                             v4f* part, v4f (&acc)[MI][NJ]) {
+  constexpr bool TWO = 128 % (16 * NJ) != 0;  // a workgroup can cross a scale block
   const int lane = threadIdx.x & 63, ks = wave_id();
   const int nmine = ks < nkb ? (nkb - ks + 3) / 4 : 0;  // K blocks this wave adds
   // the t-th K block of this wave; t past the end repeats its last block
@@ -1110,7 +1129,7 @@ __device__ __forceinline__ bool stream_rows(const uint8_t* const (&aline)[MI][2]
 
   Raw16g wr[D][NJ];
   Lines2 ar[D][MI];
-  float sar[D][MI], swr[D];
+  float sar[D][MI], swr[D], swr2[D];
   auto fetch = [&](int sl, int kb) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) wr[sl][j] = wload(j, kb);
@@ -1119,7 +1138,8 @@ __device__ __forceinline__ bool stream_rows(const uint8_t* const (&aline)[MI][2]
       ar[sl][i] = load_lines(aline[i][0] + (int64_t)kb * kBK, aline[i][1] + (int64_t)kb * kBK);
       sar[sl][i] = sarow[i][kb];
     }
-    swr[sl] = swrow[kb];
+    swr[sl] = ws.lo[kb];
+    if constexpr (TWO) swr2[sl] = ws.hi[kb];
   };
   // the ring slots are compile-time indices (the ring stays in registers)
   auto each_slot = [&](auto f) {
@@ -1154,7 +1174,7 @@ __device__ __forceinline__ bool stream_rows(const uint8_t* const (&aline)[MI][2]
 #pragma unroll
           for (int i = 0; i < MI; ++i) {
             const v4f pr = block_product(wf, xf[i], zero);
-            const float sc = sar[sl][i] * swr[sl];
+            const float sc = sar[sl][i] * (TWO && j >= ws.split ? swr2[sl] : swr[sl]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[r], sc, acc[i][j][r]);
           }
@@ -1222,19 +1242,19 @@ __global__ __launch_bounds__(256) void decode_gemm_kernel(
     for (int q = 0; q < 2; ++q)
       aline[i][q] = A + (int64_t)min(16 * i + 8 * q + (lane >> 3), M - 1) * lda + 16 * (lane & 7);
   }
-  const float* swrow = SW + (int64_t)(n0 / 128) * nkb;
+  const WScales ws = wscales_of(SW, n0, N, nkb);
   v4f acc[MI][NJ];
   bool mine;
   if (PK) {
     const int64_t cs = (int64_t)(N / 16) * 1024;
     const uint8_t* wl = W + (int64_t)(n0 / 16) * 1024 + 16 * (threadIdx.x & 63);
     mine = stream_rows<MI, NJ, D>(aline, sarow, [&](int j, int kb) { return load_frag_packed(wl, cs, j, kb); },
-                                  swrow, nkb, lds_a, part, acc);
+                                  ws, nkb, lds_a, part, acc);
   } else {
     const uint8_t* wrow = W + (int64_t)(n0 + l16) * ldw;
     mine = stream_rows<MI, NJ, D>(
         aline, sarow, [&](int j, int kb) { return load_frag_global(wrow + (int64_t)16 * j * ldw + (int64_t)kb * kBK); },
-        swrow, nkb, lds_a, part, acc);
+        ws, nkb, lds_a, part, acc);
   }
   if (!mine) return;
   stream_store<MI, BF16, NJ>(Y, acc, n0, [&](int r) -> int64_t { return r < M ? (int64_t)r * ldy : -1; });
@@ -1417,7 +1437,7 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
         const uint8_t* wrow = PK ? W + (int64_t)e * N * K + (int64_t)(n0 / 16) * 1024 + 16 * lane
                                  : W + ((int64_t)e * N + n0 + l16) * K;
         const int64_t cs = (int64_t)(N / 16) * 1024;
-        const float* swrow = SW + ((int64_t)e * (N / 128) + n0 / 128) * nkb;
+        const WScales ws = wscales_of(SW + (int64_t)e * (N / 128) * nkb, n0, N, nkb);
         v4f* part = reinterpret_cast<v4f*>(lds0);
         auto row_off = [&](int r) -> int64_t { return r < t ? (int64_t)(r0 + r) * N : -1; };
         auto run = [&](auto mi) {
@@ -1436,11 +1456,11 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void grouped_gemm_kernel(
           bool mine;
           if (PK)
             mine = stream_rows<MI>(aline, sarow, [&](int j, int kb) { return load_frag_packed(wrow, cs, j, kb); },
-                                   swrow, nkb, lds1, part, acc);
+                                   ws, nkb, lds1, part, acc);
           else
             mine = stream_rows<MI>(aline, sarow, [&](int j, int kb) {
               return load_frag_global(wrow + (int64_t)16 * j * K + (int64_t)kb * kBK);
-            }, swrow, nkb, lds1, part, acc);
+            }, ws, nkb, lds1, part, acc);
           if (mine) stream_store<MI, BF16>(Y, acc, n0, row_off);
         };
         if (t <= 16)
@@ -1560,20 +1580,37 @@ static void launch_decode_nj(const uint8_t* a, int64_t lda, const float* sa, con
                        (int)M, (int)N, (int)K, y, ldy);
 }
 
+// One or two subtiles on packed weights whose 16-row panels split evenly
+// into workgroups of 7 panels per CU (N = 28672 on 256 CUs: 256 workgroups
+// of 112 rows, where 64-row workgroups leave 192 CUs with two and 64 with
+// one): measured back to back on MI355X at 8192 -> 28672, M 1 / 8 / 32 took
+// 39.2 / 39.2 / 42.0 us against 40.2 / 41.2 / 43.2.
+#ifndef FP8B_DEC_EVEN_NJ
+#define FP8B_DEC_EVEN_NJ 7
+#endif
 template <int MI, bool PK>
 static void launch_decode(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
                           const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
                           hipStream_t s) {
-  if constexpr (!PK)  // row-major weights: two loads per 128-byte line, a 2-deep ring
+  if constexpr (!PK) {  // row-major weights: two loads per 128-byte line, a 2-deep ring
     launch_decode_nj<MI, PK, 4, 2>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
-  else if constexpr (MI == 1)
-    launch_decode_nj<1, PK, FP8B_DEC1>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
-  else if constexpr (MI == 2)
-    launch_decode_nj<2, PK, FP8B_DEC2>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
-  else if constexpr (MI == 3)
-    launch_decode_nj<3, PK, FP8B_DEC3>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
-  else
-    launch_decode_nj<4, PK, FP8B_DEC4>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+  } else {
+    constexpr int EV = FP8B_DEC_EVEN_NJ;
+    if constexpr (MI <= 2 && EV > 0) {
+      if ((N / 16) % (EV * (int64_t)cu_count(s)) == 0) {
+        launch_decode_nj<MI, PK, EV, MI == 1 ? 2 : 1>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+        return;
+      }
+    }
+    if constexpr (MI == 1)
+      launch_decode_nj<1, PK, FP8B_DEC1>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+    else if constexpr (MI == 2)
+      launch_decode_nj<2, PK, FP8B_DEC2>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+    else if constexpr (MI == 3)
+      launch_decode_nj<3, PK, FP8B_DEC3>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+    else
+      launch_decode_nj<4, PK, FP8B_DEC4>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+  }
 }
 
 template <class C, bool PK, bool M32 = false>

@@ -152,6 +152,25 @@ def test_linear_step_graph_replay_matches_eager(F, M):
         assert torch.equal(y.view(torch.int16), want.view(torch.int16)), f"replay {r}"
 
 
+@pytest.mark.parametrize("M", [1, 16, 17, 32])
+@pytest.mark.parametrize("fmt,out", [("ue8m0", torch.bfloat16), ("fp32", torch.float32)])
+def test_block_gemm_decode_panels_split_evenly(F, orc, M, fmt, out):
+    """N = 28672 packed weights: 1792 panels of 16 rows, 7 per CU on 256 CUs,
+    so one and two 16-token subtiles run 112-row workgroups (elsewhere 64);
+    K 640 (5 K blocks over the 4 waves); every output element."""
+    N, K = 28672, 640
+    c = W.decode_linear(K=K, N=N, seed=3 * M + 1)
+    fi = {"fp32": 0, "ue8m0": 1}[fmt]
+    a, sa = F.fp8_act_quant(c.x[:M].to(DEV), 128, fmt)
+    wq, ws = F.fp8_weight_quant(c.w.to(DEV), fmt)
+    y = F.fp8_block_gemm_packed(a, sa, F.fp8_weight_pack(wq), ws, out)
+    torch.cuda.synchronize()
+    oa, osa = orc.act_quant(W.bits(c.x[:M]), 128, fi)
+    ow, osw = orc.weight_quant(W.bits(c.w), fi)
+    yr, bnd = orc.block_gemm(oa, osa, ow, osw)
+    assert_parity(_np(y), yr, bnd, out == torch.bfloat16, f"{M}x{N}x{K} {fmt}")
+
+
 def test_block_gemm_decode_full(F, orc):
     """8192 -> 28672 at every decode size and across the path switches
     (streaming up to 64 tokens, then 128 x 128 tiles), both weight
