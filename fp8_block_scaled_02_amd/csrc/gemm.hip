@@ -1588,6 +1588,13 @@ static void launch_decode_nj(const uint8_t* a, int64_t lda, const float* sa, con
 #ifndef FP8B_DEC_EVEN_NJ
 #define FP8B_DEC_EVEN_NJ 7
 #endif
+// Ring depths for them (3 and 2 measured 3.5-7% slower):
+#ifndef FP8B_DEC_EVEN_D1
+#define FP8B_DEC_EVEN_D1 2  // one subtile
+#endif
+#ifndef FP8B_DEC_EVEN_D2
+#define FP8B_DEC_EVEN_D2 1  // two subtiles
+#endif
 template <int MI, bool PK>
 static void launch_decode(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
                           const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
@@ -1598,7 +1605,8 @@ static void launch_decode(const uint8_t* a, int64_t lda, const float* sa, const 
     constexpr int EV = FP8B_DEC_EVEN_NJ;
     if constexpr (MI <= 2 && EV > 0) {
       if ((N / 16) % (EV * (int64_t)cu_count(s)) == 0) {
-        launch_decode_nj<MI, PK, EV, MI == 1 ? 2 : 1>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+        launch_decode_nj<MI, PK, EV, MI == 1 ? FP8B_DEC_EVEN_D1 : FP8B_DEC_EVEN_D2>(a, lda, sa, w, ldw, sw, M, N, K,
+                                                                                   y, ldy, out_bf16, s);
         return;
       }
     }
