@@ -1021,8 +1021,9 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void mx_gemm_kernel(
 // ---- streaming few-row block GEMM -------------------------------------------
 // With few activation rows (decode, small MoE experts) a layer streams W once
 // from HBM and the math is small, so this path is built for bandwidth.  A
-// workgroup owns 64 weight rows (4 subtiles of 16 per wave) and up to 16*MI
-// activation rows; its 4 waves take every 4th K block, so together they read
+// workgroup owns 64 weight rows (4 subtiles of 16 per wave; 112 rows, 7
+// subtiles, where that splits the layer evenly over the CUs) and up to
+// 16*MI activation rows; its 4 waves take every 4th K block, so together they read
 // contiguous 512-byte runs of each weight row (one contiguous front in the
 // packed layout).  Each wave loads its weight fragments straight from
 // global memory into a register ring kStreamDepth K blocks ahead (no
