@@ -19,10 +19,11 @@ int grouped_check(const uint8_t* a, const float* a_scales, int64_t T, const int3
                   const int32_t* expert_offsets, int64_t R, int64_t E, const uint8_t* w, const float* w_scales,
                   int64_t N, int64_t K, void* y, int out_dtype) {
   if (out_dtype != FP8B_OUT_F32 && out_dtype != FP8B_OUT_BF16) return FP8B_EUNSUPPORTED;
-  if (!a || !a_scales || !row_index || !expert_offsets || !w || !w_scales || !y) return FP8B_EINVAL;
   if (T < 1 || R < 0 || E < 1 || E > 1024 || N <= 0 || K <= 0) return FP8B_EINVAL;
   if (T > kMaxDim || R > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8B_EINVAL;
   if (N % 128 != 0 || K % 128 != 0) return FP8B_EINVAL;
+  if (R == 0) return FP8B_OK;  // no routed rows: nothing is read or written
+  if (!a || !a_scales || !row_index || !expert_offsets || !w || !w_scales || !y) return FP8B_EINVAL;
   // the in-kernel work map counts tile items (128 x 128) and stream items
   // (64 weight rows) in 32-bit integers
   if ((R / 128 + E) * (N / 128) + E * (N / 64) >= INT32_MAX) return FP8B_EINVAL;
@@ -59,13 +60,13 @@ FP8B_EXPORT int fp8_act_quant(const void* x, int64_t M, int64_t K, int64_t ld_x,
   if (block_k != 128 && block_k != 32) return FP8B_EUNSUPPORTED;
   if (scale_fmt < FP8B_SCALE_FP32 || scale_fmt > FP8B_SCALE_E8M0_BYTE) return FP8B_EUNSUPPORTED;
   if (scale_fmt == FP8B_SCALE_E8M0_BYTE && block_k != 32) return FP8B_EUNSUPPORTED;
-  if (!x || !q || !scales) return FP8B_EINVAL;
   if (M < 0 || K <= 0 || M > kMaxDim || K > kMaxDim || K % block_k != 0) return FP8B_EINVAL;
   if (ld_x < K || ld_q < K) return FP8B_EINVAL;
+  if (M == 0) return FP8B_OK;  // nothing is read or written; empty arrays may be NULL
+  if (!x || !q || !scales) return FP8B_EINVAL;
   if (!aligned(x, 16) || ld_x % 8 != 0 || !aligned(q, 8) || ld_q % 8 != 0) return FP8B_EALIGN;
   if (scale_fmt != FP8B_SCALE_E8M0_BYTE && !aligned(scales, 4)) return FP8B_EALIGN;
   if (M * (K / 8) / 512 >= INT32_MAX) return FP8B_EINVAL;
-  if (M == 0) return FP8B_OK;
   return fp8blk::launch_act_quant(x, M, K, ld_x, block_k, scale_fmt, q, ld_q, scales, as_stream(stream));
 }
 
@@ -84,14 +85,14 @@ FP8B_EXPORT int fp8_block_gemm(const uint8_t* a, int64_t ld_a, const float* a_sc
                    const float* w_scales, int64_t M, int64_t N, int64_t K, void* y, int64_t ld_y, int out_dtype,
                    void* stream) {
   if (out_dtype != FP8B_OUT_F32 && out_dtype != FP8B_OUT_BF16) return FP8B_EUNSUPPORTED;
-  if (!a || !a_scales || !w || !w_scales || !y) return FP8B_EINVAL;
   if (M < 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8B_EINVAL;
   if (N % 128 != 0 || K % 128 != 0 || ld_a < K || ld_w < K || ld_y < N) return FP8B_EINVAL;
   if (ld_a >= kMaxLd || ld_w >= kMaxLd) return FP8B_EINVAL;
+  if (M == 0) return FP8B_OK;  // nothing is read or written; empty arrays may be NULL
+  if (!a || !a_scales || !w || !w_scales || !y) return FP8B_EINVAL;
   if (!aligned(a, 16) || !aligned(w, 16) || ld_a % 16 != 0 || ld_w % 16 != 0) return FP8B_EALIGN;
   if (!aligned(a_scales, 4) || !aligned(w_scales, 4) || !aligned(y, 16) || ld_y % 8 != 0) return FP8B_EALIGN;
   if (((M + 127) / 128) * (N / 128) >= INT32_MAX) return FP8B_EINVAL;
-  if (M == 0) return FP8B_OK;
   return fp8blk::launch_block_gemm(a, ld_a, a_scales, w, ld_w, w_scales, M, N, K, y, ld_y,
                                    out_dtype == FP8B_OUT_BF16, false, as_stream(stream));
 }
@@ -112,27 +113,27 @@ FP8B_EXPORT int fp8_block_gemm_packed(const uint8_t* a, int64_t ld_a, const floa
                                       const float* w_scales, int64_t M, int64_t N, int64_t K, void* y, int64_t ld_y,
                                       int out_dtype, void* stream) {
   if (out_dtype != FP8B_OUT_F32 && out_dtype != FP8B_OUT_BF16) return FP8B_EUNSUPPORTED;
-  if (!a || !a_scales || !w_packed || !w_scales || !y) return FP8B_EINVAL;
   if (M < 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxPackedN || K > kMaxDim) return FP8B_EINVAL;
   if (N % 128 != 0 || K % 128 != 0 || ld_a < K || ld_y < N || ld_a >= kMaxLd) return FP8B_EINVAL;
+  if (M == 0) return FP8B_OK;  // nothing is read or written; empty arrays may be NULL
+  if (!a || !a_scales || !w_packed || !w_scales || !y) return FP8B_EINVAL;
   if (!aligned(a, 16) || !aligned(w_packed, 16) || ld_a % 16 != 0) return FP8B_EALIGN;
   if (!aligned(a_scales, 4) || !aligned(w_scales, 4) || !aligned(y, 16) || ld_y % 8 != 0) return FP8B_EALIGN;
   if (((M + 127) / 128) * (N / 128) >= INT32_MAX) return FP8B_EINVAL;
-  if (M == 0) return FP8B_OK;
   return fp8blk::launch_block_gemm(a, ld_a, a_scales, w_packed, 0, w_scales, M, N, K, y, ld_y,
                                    out_dtype == FP8B_OUT_BF16, true, as_stream(stream));
 }
 
 FP8B_EXPORT int mxfp8_gemm(const uint8_t* a, int64_t ld_a, const uint8_t* a_e8m0, const uint8_t* b, int64_t ld_b,
                const uint8_t* b_e8m0, int64_t M, int64_t N, int64_t K, float* y, int64_t ld_y, void* stream) {
-  if (!a || !a_e8m0 || !b || !b_e8m0 || !y) return FP8B_EINVAL;
   if (M < 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8B_EINVAL;
   if (N % 128 != 0 || K % 128 != 0 || ld_a < K || ld_b < K || ld_y < N) return FP8B_EINVAL;
   if (ld_a >= kMaxLd || ld_b >= kMaxLd) return FP8B_EINVAL;
+  if (M == 0) return FP8B_OK;  // nothing is read or written; empty arrays may be NULL
+  if (!a || !a_e8m0 || !b || !b_e8m0 || !y) return FP8B_EINVAL;
   if (!aligned(a, 16) || !aligned(b, 16) || ld_a % 16 != 0 || ld_b % 16 != 0) return FP8B_EALIGN;
   if (!aligned(a_e8m0, 4) || !aligned(b_e8m0, 4) || !aligned(y, 16) || ld_y % 4 != 0) return FP8B_EALIGN;
   if (((M + 127) / 128) * (N / 128) >= INT32_MAX) return FP8B_EINVAL;
-  if (M == 0) return FP8B_OK;
   return fp8blk::launch_mx_gemm(a, ld_a, a_e8m0, b, ld_b, b_e8m0, M, N, K, y, ld_y, as_stream(stream));
 }
 
@@ -172,33 +173,33 @@ FP8B_EXPORT int fp8_weight_dequant(const uint8_t* q, int64_t N, int64_t K, int64
 FP8B_EXPORT int fp8_moe_combine(const void* y, int64_t R, int64_t N, const int32_t* token_rows, const float* gates,
                                 int64_t T, int64_t topk, void* out, int out_dtype, void* stream) {
   if (out_dtype != FP8B_OUT_F32 && out_dtype != FP8B_OUT_BF16) return FP8B_EUNSUPPORTED;
-  if (!y || !token_rows || !gates || !out) return FP8B_EINVAL;
-  if (R < 1 || R > kMaxDim || N <= 0 || N > kMaxDim || N % 8 != 0 || T < 0 || T > kMaxDim) return FP8B_EINVAL;
+  if (R < 0 || R > kMaxDim || N <= 0 || N > kMaxDim || N % 8 != 0 || T < 0 || T > kMaxDim) return FP8B_EINVAL;
   if (topk < 1 || topk > 64) return FP8B_EINVAL;
+  if (T == 0) return FP8B_OK;  // nothing is read or written; empty arrays may be NULL
+  if (R < 1 || !y || !token_rows || !gates || !out) return FP8B_EINVAL;
   if (!aligned(y, 16) || !aligned(out, 16) || !aligned(token_rows, 4) || !aligned(gates, 4)) return FP8B_EALIGN;
   if (T * (N / 8) / 256 >= INT32_MAX) return FP8B_EINVAL;
-  if (T == 0) return FP8B_OK;
   return fp8blk::launch_moe_combine(y, R, N, token_rows, gates, T, topk, out, out_dtype == FP8B_OUT_BF16,
                                     as_stream(stream));
 }
 
 FP8B_EXPORT int fp8_kv_quant(const void* x, int64_t T, int64_t D, int64_t ld_x, uint8_t* q, int64_t ld_q, float* scales,
                              void* stream) {
-  if (!x || !q || !scales) return FP8B_EINVAL;
   if (T < 0 || T > kMaxDim || D <= 0 || D > 16384 || D % 16 != 0 || ld_x < D || ld_q < D) return FP8B_EINVAL;
+  if (T == 0) return FP8B_OK;  // nothing is read or written; empty arrays may be NULL
+  if (!x || !q || !scales) return FP8B_EINVAL;
   if (!aligned(x, 16) || ld_x % 8 != 0 || !aligned(q, 8) || ld_q % 8 != 0 || !aligned(scales, 4))
     return FP8B_EALIGN;
-  if (T == 0) return FP8B_OK;
   return fp8blk::launch_kv_quant(x, T, D, ld_x, q, ld_q, scales, as_stream(stream));
 }
 
 FP8B_EXPORT int fp8_kv_dequant(const uint8_t* q, int64_t T, int64_t D, int64_t ld_q, const float* scales, void* out,
                                int64_t ld_out, void* stream) {
-  if (!q || !scales || !out) return FP8B_EINVAL;
   if (T < 0 || T > kMaxDim || D <= 0 || D > 16384 || D % 16 != 0 || ld_q < D || ld_out < D) return FP8B_EINVAL;
+  if (T == 0) return FP8B_OK;  // nothing is read or written; empty arrays may be NULL
+  if (!q || !scales || !out) return FP8B_EINVAL;
   if (!aligned(q, 16) || ld_q % 16 != 0 || !aligned(out, 16) || ld_out % 8 != 0 || !aligned(scales, 4))
     return FP8B_EALIGN;
-  if (T == 0) return FP8B_OK;
   return fp8blk::launch_kv_dequant(q, T, D, ld_q, scales, out, ld_out, as_stream(stream));
 }
 
@@ -223,10 +224,10 @@ FP8B_EXPORT int fp8_delayed_quant(const void* x, int64_t n, void* state, int64_t
 
 FP8B_EXPORT int fp8_cast_f32(const float* x, int64_t n, int fmt, uint8_t* q, void* stream) {
   if (fmt != FP8B_FMT_E4M3 && fmt != FP8B_FMT_E5M2) return FP8B_EUNSUPPORTED;
-  if (!x || !q || n < 0) return FP8B_EINVAL;
+  if (n < 0 || n / 1024 >= INT32_MAX) return FP8B_EINVAL;
+  if (n == 0) return FP8B_OK;  // nothing is read or written; empty arrays may be NULL
+  if (!x || !q) return FP8B_EINVAL;
   if (!aligned(x, 4)) return FP8B_EALIGN;
-  if (n / 1024 >= INT32_MAX) return FP8B_EINVAL;
-  if (n == 0) return FP8B_OK;
   return fp8blk::launch_cast(x, n, fmt, q, as_stream(stream));
 }
 

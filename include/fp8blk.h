@@ -27,6 +27,9 @@
  *    accepted, not that the kernel finished.
  *  - Arguments are validated on the host before anything is enqueued; a
  *    negative status means nothing was launched (except FP8B_ELAUNCH).
+ *  - Where a call allows an empty dimension (M, T, R or n = 0), it reads
+ *    and writes nothing and returns FP8B_OK once its sizes and enum values
+ *    are valid; the pointers of the empty arrays may then be NULL.
  *  - Matrices are row-major with a leading dimension `ld_*` in elements.
  *    "Codes" are E4M3 (OCP, no Inf, largest finite 448) bytes.
  *  - Scale d is the dequantisation multiplier: x ~= d * value(code).

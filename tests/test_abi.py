@@ -217,6 +217,32 @@ def test_packed_validation(L):
     assert g(*bad) == 0
 
 
+def test_empty_calls_read_nothing_and_accept_null(L):
+    """An empty dimension makes a call a no-op: the empty arrays may be NULL
+    (as torch gives for zero-size tensors), while sizes and enum values are
+    still checked."""
+    assert L.fp8_act_quant(NULL, 0, 256, 256, 128, 0, NULL, 256, NULL, NULL) == 0
+    assert L.fp8_act_quant(NULL, 0, 200, 256, 128, 0, NULL, 256, NULL, NULL) == -1    # K % 128
+    assert L.fp8_act_quant(NULL, 0, 256, 256, 64, 0, NULL, 256, NULL, NULL) == -3     # block 64
+    assert L.fp8_block_gemm(NULL, 256, NULL, NULL, 256, NULL, 0, 256, 256, NULL, 256, 1, NULL) == 0
+    assert L.fp8_block_gemm(NULL, 256, NULL, NULL, 256, NULL, 0, 200, 256, NULL, 256, 1, NULL) == -1
+    assert L.fp8_block_gemm(NULL, 256, NULL, NULL, 256, NULL, 0, 256, 256, NULL, 256, 3, NULL) == -3
+    assert L.fp8_block_gemm_packed(NULL, 256, NULL, NULL, NULL, 0, 256, 256, NULL, 256, 1, NULL) == 0
+    assert L.mxfp8_gemm(NULL, 256, NULL, NULL, 256, NULL, 0, 256, 256, NULL, 256, NULL) == 0
+    assert L.mxfp8_gemm(NULL, 256, NULL, NULL, 256, NULL, 0, 256, 100, NULL, 256, NULL) == -1
+    for g in (L.fp8_grouped_gemm, L.fp8_grouped_gemm_packed):
+        assert g(NULL, NULL, 16, NULL, NULL, 0, 4, NULL, NULL, 256, 256, NULL, 1, NULL) == 0
+        assert g(NULL, NULL, 16, NULL, NULL, 0, 0, NULL, NULL, 256, 256, NULL, 1, NULL) == -1   # E = 0
+        assert g(NULL, NULL, 16, NULL, NULL, 0, 4, NULL, NULL, 256, 256, NULL, 9, NULL) == -3
+    assert L.fp8_moe_combine(NULL, 0, 256, NULL, NULL, 0, 8, NULL, 1, NULL) == 0
+    assert L.fp8_moe_combine(NULL, 0, 256, NULL, NULL, 4, 8, NULL, 1, NULL) == -1      # rows to gather, R = 0
+    assert L.fp8_kv_quant(NULL, 0, 1024, 1024, NULL, 1024, NULL, NULL) == 0
+    assert L.fp8_kv_dequant(NULL, 0, 1024, 1024, NULL, NULL, 1024, NULL) == 0
+    assert L.fp8_kv_quant(NULL, 0, 1000, 1024, NULL, 1024, NULL, NULL) == -1          # D % 16
+    assert L.fp8_cast_f32(NULL, 0, 0, NULL, NULL) == 0
+    assert L.fp8_cast_f32(NULL, 0, 7, NULL, NULL) == -3
+
+
 def test_mfma_loop_validation(L):
     f = L.fp8b_mfma_loop
     assert f(2, GOOD, 1, 1, GOOD, NULL) == -3              # unknown kind
