@@ -17,11 +17,12 @@
 //    that misses an fp32-accumulation error budget.  E4M3 -> bf16 is exact,
 //    and the bf16 MFMA accumulates products at fp32 precision, so the codes
 //    stay FP8 in HBM and LDS (the bytes the method saves) and are widened in
-//    registers (v_cvt_scalef32_pk_bf16_fp8) right before
-//    v_mfma_f32_16x16x32_bf16.
-//  * One K step is one 128-wide scale block: four chained bf16 MFMAs give
-//    the block's partial product P in fp32, then the VALU folds it in with
-//    one FMA per output: acc += P * (sa * sw).  MX scales are powers of two
+//    registers (v_cvt_scalef32_pk_bf16_fp8) right before the bf16 MFMAs:
+//    v_mfma_f32_32x32x16_bf16 on the 128 x 128 tiles, 16x16x32 elsewhere.
+//  * One K step is one 128-wide scale block: chained bf16 MFMAs give the
+//    block's partial product P in fp32, then the VALU folds it in with one
+//    FMA per output, acc += P * (sa * sw), spread over the next block's
+//    MFMAs on the 32 x 32 step.  MX scales are powers of two
 //    and are folded into the conversion instead, so the MX loop accumulates
 //    straight in the MFMAs (tiles whose scale bytes would push a widened
 //    code out of bf16's normal range take an exact per-32-block path).
@@ -38,7 +39,9 @@
 //    scales ride along with dword direct loads into the same LDS buffer.
 //  * Two LDS buffers declared as separate arrays (so the compiler can see
 //    that the prefetch target never aliases the buffer being read), one
-//    barrier per K step.
+//    barrier per K step.  A grid of at most one 128 x 128 tile per CU
+//    (65 .. 128 tokens at decode widths) splits each tile's K blocks between
+//    two 4-wave groups of one workgroup, each with its own two buffers.
 //  * Tile order is remapped so that each XCD (8 per chip, each with its own
 //    L2) works on a contiguous, grouped patch of output tiles.
 //  * Weights may also come in a packed layout (1 KB chunks of 16 rows x 64
@@ -47,6 +50,9 @@
 //  * Up to 64 tokens (decode, the short tails of MoE experts) the weights
 //    are streamed once through registers instead of being tiled through LDS
 //    (stream_rows), the K range split over the workgroup's four waves.
+//  * The grouped GEMM's persistent grid is two halves of different order
+//    (tile items first / stream items first) whose workgroups pair up on
+//    the CUs.
 #include <algorithm>
 #include <type_traits>
 
