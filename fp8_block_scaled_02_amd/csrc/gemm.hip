@@ -103,10 +103,13 @@ struct Cfg {
   static_assert(S * BUF * KS <= 160 * 1024, "LDS capacity");
 };
 
-// LDS byte offset of logical 16-byte chunk `ch` (0..7) of tile row `r` (the
-// chunks of a row are XOR-swizzled by the row's low 3 bits, which keeps the
-// 16 x 16 fragment reads conflict-free).
-__device__ __forceinline__ int lds_off(int r, int ch) { return r * 128 + ((ch ^ (r & 7)) << 4); }
+// XOR key of tile row r.  LDS serves a 16-byte-per-lane read 16 lanes at a
+// time over 256 bytes of banks, i.e. two 128-byte rows, so 16 consecutive
+// rows read at one logical chunk hit distinct banks only if the key takes
+// 8 distinct values over the even rows and over the odd rows: bits 1-3.
+__device__ __forceinline__ int row_key(int r) { return (r >> 1) & 7; }
+// LDS byte offset of logical 16-byte chunk `ch` (0..7) of tile row `r`.
+__device__ __forceinline__ int lds_off(int r, int ch) { return r * 128 + ((ch ^ row_key(r)) << 4); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -180,17 +183,17 @@ struct Src {
 // of the stage (A groups first, then W groups).  An A group (and a W group
 // of row-major weights) is tile rows 8q .. 8q+7: lane l covers row
 // 8q + (l >> 3) and LDS position (l & 7), which holds logical chunk
-// (l & 7) ^ (row & 7) = (l & 7) ^ (l >> 3).  arow_off(r) is the byte offset
+// (l & 7) ^ row_key(row).  arow_off(r) is the byte offset
 // of activation row r from abase; woff(qw, lane) that of lane's 16 bytes of
 // W group qw from wbase (row_major_woff or packed_woff).
 template <class C, class ARow, class WOff>
 __device__ __forceinline__ void make_code_src(Src<C>& s, ARow arow_off, WOff woff) {
   const int lane = threadIdx.x & 63, wave = wave_of<C>();
-  const uint32_t chunk = (uint32_t)((lane & 7) ^ (lane >> 3));
 #pragma unroll
   for (int i = 0; i < C::NI; ++i) {
-    const int q = wave + C::NW * i;
-    s.code[i] = q < C::BM / 8 ? arow_off(8 * q + (lane >> 3)) + chunk * 16u : woff(q - C::BM / 8, lane);
+    const int q = wave + C::NW * i, row = 8 * q + (lane >> 3);
+    const uint32_t chunk = (uint32_t)((lane & 7) ^ row_key(row));
+    s.code[i] = q < C::BM / 8 ? arow_off(row) + chunk * 16u : woff(q - C::BM / 8, lane);
   }
 }
 
@@ -198,7 +201,7 @@ __device__ __forceinline__ void make_code_src(Src<C>& s, ARow arow_off, WOff wof
 // swizzled row layout of the A groups.
 __device__ __forceinline__ uint32_t row_major_woff(int qw, int lane, int64_t ld) {
   const int r = 8 * qw + (lane >> 3);
-  return (uint32_t)(r * ld) + (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+  return (uint32_t)(r * ld) + (uint32_t)(((lane & 7) ^ row_key(r)) * 16);
 }
 
 // ---- packed weight layout ---------------------------------------------------
@@ -563,11 +566,11 @@ __device__ __forceinline__ void epilogue(void* __restrict__ y, const v4f (&acc)[
 // K bytes 64h .. 64h+63 of the 128-wide K block: MFMA kk (0..7) multiplies
 // bytes 64h + 8kk .. +7 of both operands, so every K of the block is
 // multiplied exactly once.  Each lane reads 16 bytes (two MFMAs' worth) of a
-// fragment per ds_read_b128.  Packed weight chunks read conflict-free; 32
-// consecutive XOR-swizzled activation rows in a 32-lane half cost about 4
-// LDS bank-conflict cycles per read on MI355X, one per MFMA.  Storing the
-// activation tile in the packed chunk order instead removes them, but its
-// half-line (64-byte) global loads made the prefill GEMM 10% slower.
+// fragment per ds_read_b128.  Both read conflict-free: packed weight chunks
+// are 256 contiguous bytes per 16 lanes, and the activation rows' XOR key
+// (row_key, bits 1-3 of the row) spreads 16 consecutive rows over all the
+// banks.  Keyed on bits 0-2 instead, rows r and r + 8 shared banks: about 4
+// conflict cycles per read, 0.9% of the prefill GEMM's time.
 //
 // The four 32 x 32 blocks accumulate the K block's partial P in four
 // independent MFMA chains; P is folded into acc (acc += P * sa * sw, one FMA
