@@ -103,10 +103,11 @@ struct Cfg {
   static_assert(S * BUF * KS <= 160 * 1024, "LDS capacity");
 };
 
-// XOR key of tile row r.  LDS serves a 16-byte-per-lane read 16 lanes at a
-// time over 256 bytes of banks, i.e. two 128-byte rows, so 16 consecutive
-// rows read at one logical chunk hit distinct banks only if the key takes
-// 8 distinct values over the even rows and over the odd rows: bits 1-3.
+// XOR key of tile row r: bits 1-3 of the row.  Measured on MI355X with the
+// LDS bank-conflict counter, every fragment read of these kernels (16 rows x
+// 4 chunks, 32 rows x 2 chunks, 8 rows x 8 chunks of 16 bytes per lane) is
+// conflict-free with it; keyed on bits 0-2, the 32-row reads of the 32 x 32
+// K step took about 4 conflict cycles per ds_read_b128.
 __device__ __forceinline__ int row_key(int r) { return (r >> 1) & 7; }
 // LDS byte offset of logical 16-byte chunk `ch` (0..7) of tile row `r`.
 __device__ __forceinline__ int lds_off(int r, int ch) { return r * 128 + ((ch ^ row_key(r)) << 4); }
@@ -567,10 +568,9 @@ __device__ __forceinline__ void epilogue(void* __restrict__ y, const v4f (&acc)[
 // bytes 64h + 8kk .. +7 of both operands, so every K of the block is
 // multiplied exactly once.  Each lane reads 16 bytes (two MFMAs' worth) of a
 // fragment per ds_read_b128.  Both read conflict-free: packed weight chunks
-// are 256 contiguous bytes per 16 lanes, and the activation rows' XOR key
-// (row_key, bits 1-3 of the row) spreads 16 consecutive rows over all the
-// banks.  Keyed on bits 0-2 instead, rows r and r + 8 shared banks: about 4
-// conflict cycles per read, 0.9% of the prefill GEMM's time.
+// are contiguous, and the activation rows carry the row_key swizzle (keyed
+// on the row's bits 0-2 instead, these 32-row reads took about 4 conflict
+// cycles each, 0.9% of the prefill GEMM's time).
 //
 // The four 32 x 32 blocks accumulate the K block's partial P in four
 // independent MFMA chains; P is folded into acc (acc += P * sa * sw, one FMA
