@@ -287,21 +287,6 @@ __device__ __forceinline__ Raw16 read_raw(const uint8_t* t, int r, int g) {
   return v;
 }
 
-// A lane's weight fragment for tile rows row0 .. row0+15 (row0 a multiple
-// of 16) from the stage's W region: swizzled rows, or packed chunks (see
-// packed_woff).
-template <class C, bool PK>
-__device__ __forceinline__ Raw16 read_w(const uint8_t* wt, int row0, int lane) {
-  if (PK) {
-    const uint8_t* p = wt + (row0 >> 4) * 1024 + 16 * lane;
-    Raw16 v;
-    v.lo = *reinterpret_cast<const uint4*>(p);
-    v.hi = *reinterpret_cast<const uint4*>(p + (C::BN / 16) * 1024);
-    return v;
-  }
-  return read_raw(wt, row0 + (lane & 15), lane >> 4);
-}
-
 __device__ __forceinline__ Frag16 widen(const Raw16& v, float s_lo, float s_hi) {
   Frag16 f;
   f.k[0] = cvt8(v.lo.x, v.lo.y, s_lo);
@@ -331,18 +316,39 @@ __device__ __forceinline__ void compute_block(const uint8_t* buf, v4f (&acc)[C::
   // fragments go out together (15 reads, the most the LDS wait counter can
   // track), later weight fragments two subtiles ahead of their use inside
   // the MFMA loop.
+  // One per-lane base per operand (as in compute_mx): activation fragment i
+  // sits 2048 * i bytes past the first, weight fragment j 2048 * j bytes
+  // (swizzled rows) or 1024 * j (packed chunks, the second K half BN/16
+  // chunks further); chunk g + 4 of a swizzled row is chunk g's offset ^ 64.
+  const int a_lo = lds_off(wm * C::TM + l16, g), a_hi = a_lo ^ 64;
+  const int w_lo = PK ? ((wn * C::TN) >> 4) * 1024 + 16 * lane : lds_off(wn * C::TN + l16, g);
+  const int w_hi = PK ? w_lo + (C::BN / 16) * 1024 : (w_lo ^ 64);
+  constexpr int w_step = PK ? 1024 : 2048;
+  auto read_a = [&](int i) {
+    Raw16 v;
+    v.lo = *reinterpret_cast<const uint4*>(buf + a_lo + 2048 * i);
+    v.hi = *reinterpret_cast<const uint4*>(buf + a_hi + 2048 * i);
+    return v;
+  };
+  auto read_wf = [&](int j) {
+    Raw16 v;
+    v.lo = *reinterpret_cast<const uint4*>(wt + w_lo + w_step * j);
+    v.hi = *reinterpret_cast<const uint4*>(wt + w_hi + w_step * j);
+    return v;
+  };
+  const float* sa_l = sa + wm * C::TM + l16;
   Raw16 wraw[C::NJ];
   Frag16 xf[C::MI];
   float s[C::MI];
   float sar[C::MI];
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i) sar[i] = sa[wm * C::TM + 16 * i + l16];
+  for (int i = 0; i < C::MI; ++i) sar[i] = sa_l[16 * i];
   const float sw0 = sw[(wn * C::TN) / 128];
   Raw16 araw[C::MI];
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i) araw[i] = read_raw(buf, wm * C::TM + 16 * i + l16, g);
+  for (int i = 0; i < C::MI; ++i) araw[i] = read_a(i);
 #pragma unroll
-  for (int j = 0; j < 2 && j < C::NJ; ++j) wraw[j] = read_w<C, PK>(wt, wn * C::TN + 16 * j, lane);
+  for (int j = 0; j < 2 && j < C::NJ; ++j) wraw[j] = read_wf(j);
   // Only the first 32-wide K window of the activation fragments is widened
   // up front; windows 1..3 are widened between the MFMAs of the first weight
   // fragment, so the step does not open with a VALU-only burst that leaves
@@ -363,7 +369,7 @@ __device__ __forceinline__ void compute_block(const uint8_t* buf, v4f (&acc)[C::
   v4f p[C::MI], prev[C::MI];
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j) {
-    if (j + 2 < C::NJ) wraw[j + 2] = read_w<C, PK>(wt, wn * C::TN + 16 * (j + 2), lane);
+    if (j + 2 < C::NJ) wraw[j + 2] = read_wf(j + 2);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
 #pragma unroll
@@ -421,21 +427,32 @@ template <class C, class Hook>
 __device__ __forceinline__ void compute_mx(const uint8_t* buf, v4f (&acc)[C::MI][C::NJ], Hook hook) {
   const int lane = threadIdx.x & 63, wave = wave_of<C>();
   const int wm = wave % C::WM, wn = wave / C::WM, l16 = lane & 15, g = lane >> 4;
-  const uint32_t* ea = reinterpret_cast<const uint32_t*>(buf + C::OFF_SA);
-  const uint32_t* eb = reinterpret_cast<const uint32_t*>(buf + C::OFF_SB);
   const int b0 = 8 * (g >> 1), b1 = 8 * (2 + (g >> 1));
+  // One per-lane base per operand: the row key repeats every 16 rows, so
+  // fragment i sits 2048 * i bytes (and its scale dword 64 * i bytes) past
+  // the first, and chunk g + 4 is chunk g's offset ^ 64; the constant parts
+  // fold into the LDS reads' offsets instead of costing VALU per K step.
+  const int a_lo = lds_off(wm * C::TM + l16, g), a_hi = a_lo ^ 64;
+  const int w_lo = C::OFF_W + lds_off(wn * C::TN + l16, g), w_hi = C::OFF_W + (lds_off(wn * C::TN + l16, g) ^ 64);
+  const uint32_t* ea = reinterpret_cast<const uint32_t*>(buf + C::OFF_SA) + wm * C::TM + l16;
+  const uint32_t* eb = reinterpret_cast<const uint32_t*>(buf + C::OFF_SB) + wn * C::TN + l16;
+  auto raw = [&](int lo, int hi, int k) {
+    Raw16 v;
+    v.lo = *reinterpret_cast<const uint4*>(buf + lo + 2048 * k);
+    v.hi = *reinterpret_cast<const uint4*>(buf + hi + 2048 * k);
+    return v;
+  };
   // reads first (A fragments, their scales, the first weight fragment),
   // then the conversions; later weight fragments one subtile ahead
   Raw16 araw[C::MI], wraw[2];
   uint32_t eav[C::MI], ebv[2];
 #pragma unroll
   for (int i = 0; i < C::MI; ++i) {
-    const int r = wm * C::TM + 16 * i + l16;
-    eav[i] = ea[r];
-    araw[i] = read_raw(buf, r, g);
+    eav[i] = ea[16 * i];
+    araw[i] = raw(a_lo, a_hi, i);
   }
-  ebv[0] = eb[wn * C::TN + l16];
-  wraw[0] = read_raw(buf + C::OFF_W, wn * C::TN + l16, g);
+  ebv[0] = eb[0];
+  wraw[0] = raw(w_lo, w_hi, 0);
   Frag16 xf[C::MI];
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
@@ -450,9 +467,8 @@ __device__ __forceinline__ void compute_mx(const uint8_t* buf, v4f (&acc)[C::MI]
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j) {
     if (j + 1 < C::NJ) {
-      const int rn = wn * C::TN + 16 * (j + 1) + l16;
-      ebv[(j + 1) & 1] = eb[rn];
-      wraw[(j + 1) & 1] = read_raw(buf + C::OFF_W, rn, g);
+      ebv[(j + 1) & 1] = eb[16 * (j + 1)];
+      wraw[(j + 1) & 1] = raw(w_lo, w_hi, j + 1);
     }
     const uint32_t e = ebv[j & 1];
     const Frag16 wf = widen(wraw[j & 1], e8m0_to_f32((e >> b0) & 0xffu), e8m0_to_f32((e >> b1) & 0xffu));
