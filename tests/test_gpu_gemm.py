@@ -263,7 +263,11 @@ def _mx_case(F, orc, a_bf, b_bf, rows=None):
     return yg, yr, bnd
 
 
-@pytest.mark.parametrize("M,N,K", [(200, 256, 512), (16, 128, 128), (130, 384, 640)])
+# (2085, 512, 384) and (2048, 256, 128) run on the 256 x 256 tiles (M >= 2048
+# and N a multiple of 256): a ragged last m-tile with an odd number of K
+# steps, and a single K step; the others on the 128 x 128 tiles.
+@pytest.mark.parametrize("M,N,K", [(200, 256, 512), (16, 128, 128), (130, 384, 640), (2085, 512, 384),
+                                   (2048, 256, 128)])
 def test_mx_gemm_small(F, orc, M, N, K):
     a, b = W.mx_case(M=M, N=N, K=K, seed=M + K)
     yg, yr, bnd = _mx_case(F, orc, a, b)
