@@ -1043,6 +1043,251 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void mx_gemm_kernel(
   epilogue<C, false>(Y, acc, n0, [&](int r) -> int64_t { return m0 + r < M ? (int64_t)(m0 + r) * ldy : -1; });
 }
 
+// ---- 1 .. 64 tokens on packed weights: weights streamed into registers ----
+// One 512-thread workgroup per 128-row weight tile (N / 128 of them, at most
+// one per CU).  Its two 4-wave groups split the K blocks (group g takes
+// blocks g, g + 2, ..., the K split of the tiled kernel), and wave w of a
+// group owns weight rows 32w .. 32w+31 of the tile against every token row
+// (MI fragments of 32 tokens).  The weights, the operand that comes from
+// HBM, never pass through LDS: each wave loads its own rows' codes of a K
+// block straight from the packed layout into a three-deep register ring,
+// two blocks ahead of their use, with no wave re-reading another's.  Only
+// the activation tile (read by every workgroup, L2-resident) and its scales
+// go through LDS, on a three-stage ring per group.
+//
+// Every wave widens all MI token fragments, so the VALU work per MFMA grows
+// with MI: at three and four fragments (65 .. 128 tokens) the kernel was
+// slower than the 128 x 128 tiles, whose waves widen half the fragments
+// (measured at 8192 -> 28672: 82 against 68 us at 128 tokens).
+//
+// Arithmetic: the same 32 x 32 x 16 MFMA chains, K assignment and fold as
+// the tiled kernel's K-split form (lane 32h + r takes K bytes 64h + 8kk ..
+// +7 of the block in MFMA window kk; each block's partial is folded as
+// acc = fma(P, sa * sw, acc) in block order; group 1's sum is added to group
+// 0's at the end), so each output row is bit-identical to the one that
+// kernel computes for the same token.
+template <int MI>
+struct WdCfg {
+  static constexpr int ROWS = 32 * MI;                  // token rows in the activation stage
+  static constexpr int NSA = (ROWS + 63) / 64;          // waves that load the token scales
+  static constexpr int OFF_SA = ROWS * 128;
+  static constexpr int OFF_SB = OFF_SA + 256 * NSA;     // one 64-lane, 4-byte DMA per scale wave
+  static constexpr int BUF = OFF_SB + 256;
+  // vector memory instructions a wave issues per K block: four weight
+  // loads, MI activation row groups, and a scale load on waves 0 .. NSA
+  static constexpr int OPS = 4 + MI;
+  static_assert(MI >= 1 && MI <= 2, "one or two token fragments");
+  static_assert(4 * MI * 2 * 64 * 16 <= 2 * BUF, "half of the K-split partials fit in one stage array");
+};
+
+// Activation source of one wave: its MI row groups (rows 8q .. 8q+7 of the
+// tile, q = w + 4i, swizzled chunk per lane) and its scale load, if any.
+template <int MI>
+struct WdSrc {
+  const uint8_t* abase;   // activation tile at this group's first K block (uniform)
+  uint32_t code[MI];      // per-lane row + chunk offsets
+  const uint8_t* sbase;   // scale row at this group's first K block (uniform)
+  uint32_t soff;          // per-lane scale offset
+  int scale_dst;          // stage offset of the scale load, or -1
+};
+
+template <int MI>
+__device__ __forceinline__ void wd_issue(uint8_t* __restrict__ buf, const WdSrc<MI>& s, int kb, int w) {
+  if (s.scale_dst >= 0) dma4(rsrc_at(s.sbase + (size_t)kb * 4), s.soff, buf + s.scale_dst);
+  const __amdgpu_buffer_rsrc_t ra = rsrc_at(s.abase + (size_t)kb * kBK);
+#pragma unroll
+  for (int i = 0; i < MI; ++i) dma16(ra, s.code[i], buf + (w + 4 * i) * 1024);
+}
+
+// The wave's 32 weight rows of K block kb: lane 32h + r holds row r, chunk
+// (2kb + h), pieces g = 0..3 (codes 64h + 16g .. +15 of the block).
+struct WdW {
+  u32x4 g[4];
+};
+
+// wbase: the wave's rows at this group's block (uniform), advanced by
+// bstride bytes per step; voff: the lane's offset from it.  Buffer loads
+// keep the base in SGPRs; the codes are read once (non-temporal).
+__device__ __forceinline__ WdW wd_load_w(const uint8_t* wbase, int64_t bstride, int t, uint32_t voff) {
+  const __amdgpu_buffer_rsrc_t rs = rsrc_at(wbase + (int64_t)t * bstride);
+  WdW v;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) v.g[g] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 256 * g, 0, 2 /* nt */);
+  return v;
+}
+
+// One K block of a wave: the partials of the MI token fragments over the
+// eight MFMA windows (the weight fragment widened window by window), then
+// the fold acc += P * sa * sw.
+template <int MI>
+__device__ __forceinline__ void wd_block(const uint8_t* __restrict__ buf, const WdW& wv, v16f (&acc)[MI], int lane) {
+  using C = WdCfg<MI>;
+  const int r = lane & 31, h = lane >> 5;
+  const int a_off = lds_off(r, 4 * h);  // token fragment i is 32 rows (4096 bytes) further
+  const float* sa = reinterpret_cast<const float*>(buf + C::OFF_SA);
+  const float sw = *reinterpret_cast<const float*>(buf + C::OFF_SB);
+  uint4 ra[2][MI];
+  auto load = [&](int sl, int kk2) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) ra[sl][i] = *reinterpret_cast<const uint4*>(buf + 4096 * i + (a_off ^ (kk2 << 4)));
+  };
+  load(0, 0);
+  v16f P[MI];
+#pragma unroll
+  for (int kk2 = 0; kk2 < 4; ++kk2) {
+    const int sl = kk2 & 1;
+    if (kk2 < 3) load(sl ^ 1, kk2 + 1);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int kk = 2 * kk2 + half;
+      const bf16x8 xw = half ? cvt8(wv.g[kk2][2], wv.g[kk2][3], 1.0f) : cvt8(wv.g[kk2][0], wv.g[kk2][1], 1.0f);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const bf16x8 xa = half ? cvt8(ra[sl][i].z, ra[sl][i].w, 1.0f) : cvt8(ra[sl][i].x, ra[sl][i].y, 1.0f);
+        P[i] = mfma32_bf16(xw, xa, kk == 0 ? v16f{} : P[i]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const float sc = sa[32 * i + r] * sw;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[i][v] = __builtin_fmaf(P[i][v], sc, acc[i][v]);
+  }
+  // the folds complete inside this block (sunk past the next barrier, they
+  // kept two blocks' partials live)
+#pragma unroll
+  for (int i = 0; i < MI; ++i) asm volatile("" : "+v"(acc[i]));
+}
+
+template <int MI, bool BF16>
+__global__ __launch_bounds__(512, 1) void wdecode_kernel(const uint8_t* __restrict__ A, int64_t lda,
+                                                         const float* __restrict__ SA, const uint8_t* __restrict__ W,
+                                                         const float* __restrict__ SW, int M, int N, int K,
+                                                         void* __restrict__ Y, int64_t ldy) {
+  using C = WdCfg<MI>;
+  // three stages per group; separate arrays, so the compiler can tell which
+  // stage every LDS read touches
+  __shared__ __attribute__((aligned(16))) uint8_t st0[2 * C::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[2 * C::BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[2 * C::BUF];
+  const int lane = threadIdx.x & 63, wid = wave_id(), group = wid >> 2, w = wid & 3;
+  const int r = lane & 31, h = lane >> 5;
+  // group g takes K blocks g, g + 2, ... (the launcher keeps their number
+  // even): step t is K block 2t + g
+  constexpr int KS = 2;  // K blocks per step
+  const int n0 = (int)blockIdx.x * 128, nkb = K / kBK, nsteps = nkb / KS, kb0 = group;
+
+  WdSrc<MI> src;
+  src.abase = A + kb0 * kBK;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int row = 8 * (w + 4 * i) + (lane >> 3);
+    src.code[i] = (uint32_t)(min(row, M - 1) * lda) + (uint32_t)(((lane & 7) ^ row_key(row)) * 16);
+  }
+  src.scale_dst = -1;
+  src.sbase = reinterpret_cast<const uint8_t*>(SA + kb0);
+  src.soff = 0;
+  if (w < C::NSA) {
+    src.soff = (uint32_t)(min(64 * w + lane, M - 1) * nkb * 4);
+    src.scale_dst = C::OFF_SA + 256 * w;
+  } else if (w == C::NSA) {
+    src.sbase = reinterpret_cast<const uint8_t*>(SW + (int64_t)(n0 / 128) * nkb + kb0);
+    src.scale_dst = C::OFF_SB;
+  }
+  const int64_t bstride = 2 * (int64_t)(N / 16) * 1024;  // packed bytes per K block
+  const uint8_t* wbase = W + (int64_t)((n0 + 32 * w) / 16) * 1024 + (int64_t)kb0 * bstride;
+  const uint32_t wvoff = (uint32_t)((h * (N / 16) + (r >> 4)) * 1024 + 16 * (r & 15));
+  uint8_t* const b0 = st0 + group * C::BUF;
+  uint8_t* const b1 = st1 + group * C::BUF;
+  uint8_t* const b2 = st2 + group * C::BUF;
+
+  v16f acc[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) acc[i] = v16f{};
+  WdW w0, w1, w2;
+  // step t (K block KS t + kb0): activation stage and weight slot t % 3
+  w0 = wd_load_w(wbase, KS * bstride, 0, wvoff);
+  wd_issue<MI>(b0, src, 0, w);
+  if (nsteps > 1) {
+    w1 = wd_load_w(wbase, KS * bstride, 1, wvoff);
+    wd_issue<MI>(b1, src, KS, w);
+  }
+  // Step t: wait for this wave's loads of step t (those of step t + 1 may
+  // still fly: next_issued), barrier, issue step t + 2 into the slot and
+  // stage that step t - 1 used, compute step t.
+  auto step = [&](int t, bool next_issued, const uint8_t* cur, const WdW& wcur, uint8_t* refill, WdW& wrefill,
+                  bool issue) {
+    if (next_issued) {
+      if (w <= C::NSA) wait_vmem<C::OPS + 1>(); else wait_vmem<C::OPS>();
+    } else {
+      wait_vmem<0>();
+    }
+    // every wave's step t is in LDS, and every wave has consumed its reads
+    // of stage (t + 2) % 3 (used by its MFMAs before it got here).  A bare
+    // s_barrier: the fence of __syncthreads would make the compiler wait for
+    // step t + 1's loads too, since it cannot tell that their LDS writes go
+    // to another stage.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (issue) {
+      wrefill = wd_load_w(wbase, KS * bstride, t + 2, wvoff);
+      wd_issue<MI>(refill, src, KS * (t + 2), w);
+    }
+    wd_block<MI>(cur, wcur, acc, lane);
+  };
+  // main loop: every step refills (no loads issued under a branch, so the
+  // compiler's own waits for the weight registers stay exact across it)
+  int t = 0;
+  for (; t + 5 <= nsteps; t += 3) {
+    step(t, true, b0, w0, b2, w2, true);
+    step(t + 1, true, b1, w1, b0, w0, true);
+    step(t + 2, true, b2, w2, b1, w1, true);
+  }
+  // the last one to four steps (slots 0, 1, 2, 0)
+  step(t, t + 1 < nsteps, b0, w0, b2, w2, t + 2 < nsteps);
+  if (t + 1 < nsteps) step(t + 1, t + 2 < nsteps, b1, w1, b0, w0, t + 3 < nsteps);
+  if (t + 2 < nsteps) step(t + 2, t + 3 < nsteps, b2, w2, b1, w1, false);
+  if (t + 3 < nsteps) step(t + 3, false, b0, w0, b2, w2, false);
+
+  // group 1 leaves its sums in LDS (values 0 .. 7 of each fragment in the
+  // first stage array, 8 .. 15 in the second), group 0 adds them
+  __syncthreads();
+  auto part = [&](int i, int q) {
+    return reinterpret_cast<v4f*>(q < 2 ? st0 : st1) + ((w * MI + i) * 2 + (q & 1)) * 64 + lane;
+  };
+  if (group == 1) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *part(i, q) = v4f{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]};
+  }
+  __syncthreads();
+  if (group != 0) return;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const v4f o = *part(i, q);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[i][4 * q + v] += o[v];
+    }
+  // lane 32h + r of fragment i holds token 32i + r and weight rows
+  // 32w + 8q + 4h .. +3 in values 4q .. 4q+3
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int m = 32 * i + r;
+    if (m < M) {
+      const int64_t base = (int64_t)m * ldy + n0 + 32 * w + 4 * h;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        store4<BF16>(Y, base + 8 * q, v4f{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]});
+    }
+  }
+}
+
 // ---- streaming few-row block GEMM -------------------------------------------
 // With few activation rows (decode, small MoE experts) a layer streams W once
 // from HBM and the math is small, so this path is built for bandwidth.  A
@@ -1661,10 +1906,32 @@ static void launch_block(const uint8_t* a, int64_t lda, const float* sa, const u
                        (int)N, (int)K, y, ldy);
 }
 
+#ifndef FP8B_WDECODE_MAX_M
+#define FP8B_WDECODE_MAX_M 64  // packed weights with up to this many tokens take wdecode_kernel
+#endif
+template <int MI>
+static void launch_wdecode(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, const float* sw,
+                           int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16, hipStream_t s) {
+  const dim3 grid((unsigned)(N / 128)), block(512);
+  if (out_bf16)
+    hipLaunchKernelGGL((wdecode_kernel<MI, true>), grid, block, 0, s, a, lda, sa, w, sw, (int)M, (int)N, (int)K, y,
+                       ldy);
+  else
+    hipLaunchKernelGGL((wdecode_kernel<MI, false>), grid, block, 0, s, a, lda, sa, w, sw, (int)M, (int)N, (int)K, y,
+                       ldy);
+}
+
 template <bool PK>
 static void launch_block_any(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w, int64_t ldw,
                              const float* sw, int64_t M, int64_t N, int64_t K, void* y, int64_t ldy, int out_bf16,
                              hipStream_t s) {
+  if (PK && M <= FP8B_WDECODE_MAX_M && N / 128 <= cu_count(s) && (K / kBK) % 2 == 0) {
+    if (M <= 32)
+      launch_wdecode<1>(a, lda, sa, w, sw, M, N, K, y, ldy, out_bf16, s);
+    else
+      launch_wdecode<2>(a, lda, sa, w, sw, M, N, K, y, ldy, out_bf16, s);
+    return;
+  }
   // the streaming kernel for M <= 64 on packed weights (one to four 16-token
   // subtiles), M <= 32 on row-major ones
   if (M <= 16)

@@ -173,8 +173,9 @@ def test_block_gemm_decode_panels_split_evenly(F, orc, M, fmt, out):
 
 def test_block_gemm_decode_full(F, orc):
     """8192 -> 28672 at every decode size and across the path switches
-    (streaming up to 64 tokens, then 128 x 128 tiles), both weight
-    layouts; sampled token rows x every output column."""
+    (up to 64 tokens the register-streamed kernel on packed weights and the
+    streaming kernel or 64 x 128 tiles on row-major ones, then 128 x 128
+    tiles), both weight layouts; sampled token rows x every output column."""
     c = W.decode_linear(device=DEV)
     a, sa = F.fp8_act_quant(c.x, 128, "ue8m0")
     wq, ws = F.fp8_weight_quant(c.w, "ue8m0")
@@ -651,3 +652,47 @@ def test_gemms_with_activations_beyond_4gib(F, orc):
     assert_parity(_np(ym[rows]), yr, bnd, False, "mx gemm, rows past 4 GiB")
     del big
     torch.cuda.empty_cache()
+
+
+# ---- 1 .. 64 tokens on packed weights (weights streamed into registers) ----
+@pytest.mark.parametrize("N,K", [(128, 256), (384, 512), (256, 768), (640, 1024), (128, 1280),
+                                 (256, 1536), (384, 1792), (128, 2048), (256, 2560)])
+def test_block_gemm_register_streamed_decode(F, orc, N, K):
+    """Packed weights with at most 64 tokens, a grid of at most one 128-row
+    tile per CU and an even K-block count: one to eight and ten steps per
+    K-split group (a main loop of three and a tail of one to four steps),
+    one and two 32-token fragments with ragged last fragments, both scale
+    formats and output types; every output against the oracle."""
+    c = W.decode_linear(K=K, N=N, seed=N + K)
+    for fmt, out in (("ue8m0", torch.bfloat16), ("fp32", torch.float32)):
+        fi = {"fp32": 0, "ue8m0": 1}[fmt]
+        a, sa = F.fp8_act_quant(c.x[:64].to(DEV), 128, fmt)
+        wq, ws = F.fp8_weight_quant(c.w.to(DEV), fmt)
+        wp = F.fp8_weight_pack(wq)
+        oa, osa = orc.act_quant(W.bits(c.x[:64]), 128, fi)
+        ow, osw = orc.weight_quant(W.bits(c.w), fi)
+        yr, bnd = orc.block_gemm(oa, osa, ow, osw)
+        for M in (1, 2, 17, 31, 32, 33, 40, 63, 64):
+            y = F.fp8_block_gemm_packed(a[:M], sa[:M], wp, ws, out)
+            torch.cuda.synchronize()
+            assert_parity(_np(y), yr[:M], bnd[:M], out == torch.bfloat16, f"{M}x{N}x{K} {fmt}")
+
+
+@pytest.mark.parametrize("N,K", [(256, 1024), (28672, 8192)])
+def test_register_streamed_decode_rows_equal_the_tiled_kernel(F, N, K):
+    """Rows are independent, so y of M <= 64 tokens (the register-streamed
+    kernel) must equal, bit for bit, the first M rows of the same GEMM over
+    65 tokens (the 128 x 128 tiles in their K-split form), which compute
+    every row with the same MFMA chains and folds."""
+    c = W.decode_linear(device=DEV, K=K, N=N, seed=5)
+    a, sa = F.fp8_act_quant(c.x[:65], 128, "ue8m0")
+    wq, ws = F.fp8_weight_quant(c.w, "ue8m0")
+    wp = F.fp8_weight_pack(wq)
+    del c
+    for out in (torch.bfloat16, torch.float32):
+        ref = F.fp8_block_gemm_packed(a, sa, wp, ws, out)
+        for M in (1, 8, 32, 33, 64):
+            y = F.fp8_block_gemm_packed(a[:M], sa[:M], wp, ws, out)
+            torch.cuda.synchronize()
+            iv = torch.int16 if out == torch.bfloat16 else torch.int32
+            assert torch.equal(y.view(iv), ref[:M].view(iv)), f"M {M} {out} {N}x{K}"

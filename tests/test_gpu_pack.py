@@ -3,10 +3,12 @@
 fp8_weight_pack is a pure permutation: it must equal the oracle's
 element-by-element statement byte for byte.  The GEMMs on packed weights
 read the same fragments as on row-major weights, only from other
-addresses, so wherever both layouts run the same kernel (M <= 32, M > 64,
-the grouped GEMM) their outputs must be bit-identical; for 33 <= M <= 64
-only the packed layout streams, and both paths are checked against the
-oracle's tolerance instead."""
+addresses, so wherever both layouts run the same kernel (M > 64, the
+grouped GEMM, and M <= 32 when the packed GEMM also streams: an odd K-block
+count or more 128-row tiles than CUs) their outputs must be bit-identical.
+Elsewhere up to 64 tokens the packed layout takes its own kernels (the
+register-streamed kernel, or the streaming kernel against 64 x 128 tiles),
+and both paths are checked against the oracle's tolerance instead."""
 import numpy as np
 import pytest
 import torch
@@ -123,13 +125,13 @@ def test_block_gemm_packed_meets_oracle(F, orc, M):
 
 
 def test_block_gemm_packed_full_shapes(F):
-    """Decode (M 1, 8, 32, 128 at 8192 -> 28672, ue8m0) and prefill
-    (4096 x 7168 -> 18432, fp32 scales) at full size, as bench.py runs them."""
+    """Decode (M 128 at 8192 -> 28672, ue8m0) and prefill (4096 x 7168 ->
+    18432, fp32 scales) at full size, as bench.py runs them."""
     c = W.decode_linear(device=DEV)
     a, sa, wq, ws = _quant(F, c, "ue8m0")
     del c
     wp = F.fp8_weight_pack(wq)
-    for M in (1, 8, 32, 128):
+    for M in (128,):
         y0 = F.fp8_block_gemm(a[:M], sa[:M], wq, ws, torch.bfloat16)
         y1 = F.fp8_block_gemm_packed(a[:M], sa[:M], wp, ws, torch.bfloat16)
         torch.cuda.synchronize()
@@ -145,22 +147,24 @@ def test_block_gemm_packed_full_shapes(F):
     _same_bits(y1, y0, "prefill")
 
 
-def test_block_gemm_packed_decode_streaming_full(F, orc):
-    """M = 48 and 64 at 8192 -> 28672 (ue8m0): three and four 16-token
-    subtiles on the streaming kernel, which only the packed layout takes;
-    sampled rows against the oracle."""
+def test_block_gemm_packed_decode_full(F, orc):
+    """M = 1, 8, 32, 48 and 64 at 8192 -> 28672 (ue8m0), as bench.py runs
+    them: the register-streamed kernel on packed weights, the streaming
+    kernel or 64 x 128 tiles on row-major ones; sampled rows of both
+    against the oracle."""
     c = W.decode_linear(device=DEV)
     a, sa, wq, ws = _quant(F, c, "ue8m0")
     wp = F.fp8_weight_pack(wq)
     ow, osw = orc.weight_quant(W.bits(c.w), 1)
-    for M in (48, 64):
-        y = F.fp8_block_gemm_packed(a[:M], sa[:M], wp, ws, torch.bfloat16)
-        torch.cuda.synchronize()
-        rows = sorted({0, 17, 33, M - 1})
+    for M in (1, 8, 32, 48, 64):
+        rows = sorted({0, min(17, M - 1), min(33, M - 1), M - 1})
         oa, osa = orc.act_quant(W.bits(c.x[rows]), 128, 1)
         yr, bnd = orc.block_gemm(oa, osa, ow, osw)
-        yg = y[torch.as_tensor(rows, device=y.device)].float().cpu().numpy().astype(np.float64)
-        assert_parity(yg, yr, bnd, True, f"packed decode M={M}")
+        for name, y in (("packed", F.fp8_block_gemm_packed(a[:M], sa[:M], wp, ws, torch.bfloat16)),
+                        ("row-major", F.fp8_block_gemm(a[:M], sa[:M], wq, ws, torch.bfloat16))):
+            torch.cuda.synchronize()
+            yg = y[torch.as_tensor(rows, device=y.device)].float().cpu().numpy().astype(np.float64)
+            assert_parity(yg, yr, bnd, True, f"{name} decode M={M}")
 
 
 def _moe_inputs(F, case):
