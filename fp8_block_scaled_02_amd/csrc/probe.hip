@@ -1,7 +1,12 @@
-// probe.hip -- the MFMA-only loop behind fp8b_mfma_loop: dense matrix-core
-// work on operands held in registers, with no memory traffic, conversion or
-// rescale.  Its rate is the ceiling this part sustains for one MFMA
-// instruction, clock and power limits included, measured beside the GEMMs.
+// probe.hip -- measurement aids, not steps of the method:
+//  * the MFMA-only loop behind fp8b_mfma_loop: dense matrix-core work on
+//    operands held in registers, with no memory traffic, conversion or
+//    rescale.  Its rate is the ceiling this part sustains for one MFMA
+//    instruction, clock and power limits included, measured beside the GEMMs;
+//  * the streaming copy and the empty launch behind fp8b_stream_probe: the
+//    grid, workgroup shape, loads and stores of act_quant (128-blocks, fp32
+//    scales) without its arithmetic, and the same grid returning at once,
+//    which time act_quant's streaming rate and its launch and drain.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -61,7 +66,55 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(const uint32_t* __restri
   out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// Grid: x = row, y = segment of 256 * UNROLL 16-byte chunks of the row;
+// each thread non-temporally loads UNROLL chunks 256 apart (all before any
+// store, as act_quant does) and writes the low byte of each bf16 element as
+// its code (8-byte non-temporal stores) and 0 as the scale of each
+// 128-element block it leads.
+constexpr int kCopyUnroll = 4;  // act_quant's chunks per lane
+
+__global__ __launch_bounds__(256) void stream_copy_kernel(const uint16_t* __restrict__ x, int64_t K,
+                                                          uint8_t* __restrict__ q, float* __restrict__ scales) {
+  const int cpr = (int)(K / 8), nblk = (int)(K / 128);
+  const int64_t row = blockIdx.x;
+  const int base = (int)blockIdx.y * 256 * kCopyUnroll + (int)threadIdx.x;
+  const uint16_t* xr = x + row * K;
+  uint8_t* qr = q + row * K;
+  u32x4 raw[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int c = base + u * 256;
+    raw[u] = c < cpr ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + 8 * c)) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int c = base + u * 256;
+    if (c < cpr) {
+      u32x2 out;
+      out[0] = __builtin_amdgcn_perm(raw[u][1], raw[u][0], 0x06040200u);
+      out[1] = __builtin_amdgcn_perm(raw[u][3], raw[u][2], 0x06040200u);
+      __builtin_nontemporal_store(out, reinterpret_cast<u32x2*>(qr + 8 * c));
+      if ((c % 16) == 0) scales[row * nblk + c / 16] = 0.0f;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void empty_kernel() {}
+
 }  // namespace
+
+int launch_stream_probe(int kind, const void* x, int64_t M, int64_t K, uint8_t* q, float* scales,
+                        hipStream_t s) {
+  const int64_t cpr = K / 8;
+  const int64_t segs = (cpr + 256 * kCopyUnroll - 1) / (256 * kCopyUnroll);
+  if (segs > 65535 || M > 0x7fffffff) return FP8B_EINVAL;
+  const dim3 grid((unsigned)M, (unsigned)segs);
+  if (kind == FP8B_PROBE_COPY)
+    hipLaunchKernelGGL(stream_copy_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(x), K, q, scales);
+  else
+    hipLaunchKernelGGL(empty_kernel, grid, dim3(256), 0, s);
+  return check_launch();
+}
 
 int launch_mfma_loop(int kind, const uint32_t* ops, int64_t iters, int64_t workgroups, float* out,
                      hipStream_t s) {

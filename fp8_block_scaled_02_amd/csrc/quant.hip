@@ -23,16 +23,10 @@ namespace fp8blk {
 // row (so no index needs a division); each thread owns UNROLL chunks 256
 // apart, all loaded before any is processed (bytes in flight per lane =
 // 16 * UNROLL).
-//
-// PROBE (a measurement aid, fp8b_stream_probe): 1 moves the same bytes with
-// the same grid, loads and stores but no arithmetic (each code byte is the
-// low byte of its bf16 element, each scale 0); 2 returns at once (the
-// launch and drain of the same grid).
-template <int BLOCK, int FMT, int UNROLL, int PROBE = 0>
+template <int BLOCK, int FMT, int UNROLL>
 __global__ __launch_bounds__(256) void act_quant_kernel(
     const uint16_t* __restrict__ x, int64_t K, int64_t ldx,
     uint8_t* __restrict__ q, int64_t ldq, void* __restrict__ scales) {
-  if (PROBE == 2) return;
   constexpr int LPB = BLOCK / 8;  // lanes per quantisation block
   const int cpr = (int)(K / 8);   // 16-byte chunks per row
   const int nblk = (int)(K / BLOCK);
@@ -48,20 +42,6 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
     u32x4 v = {0, 0, 0, 0};
     if (c < cpr) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + 8 * c));
     raw[u] = make_uint4(v[0], v[1], v[2], v[3]);
-  }
-  if (PROBE == 1) {
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int c = base + u * 256;
-      if (c < cpr) {
-        u32x2 out;
-        out[0] = __builtin_amdgcn_perm(raw[u].y, raw[u].x, 0x06040200u);
-        out[1] = __builtin_amdgcn_perm(raw[u].w, raw[u].z, 0x06040200u);
-        __builtin_nontemporal_store(out, reinterpret_cast<u32x2*>(qr + 8 * c));
-        if ((c % LPB) == 0) reinterpret_cast<float*>(scales)[row * nblk + c / LPB] = 0.0f;
-      }
-    }
-    return;
   }
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
@@ -544,20 +524,6 @@ int launch_act_quant(const void* x, int64_t M, int64_t K, int64_t ldx, int block
     else FP8B_AQ(32, 2);
   }
 #undef FP8B_AQ
-  return check_launch();
-}
-
-int launch_stream_probe(int kind, const void* x, int64_t M, int64_t K, uint8_t* q, float* scales,
-                        hipStream_t s) {
-  const int64_t cpr = K / 8;
-  const int64_t segs = (cpr + 256 * kActUnroll - 1) / (256 * kActUnroll);
-  if (segs > 65535 || M > 0x7fffffff) return FP8B_EINVAL;
-  const dim3 grid((unsigned)M, (unsigned)segs);
-  const uint16_t* xp = static_cast<const uint16_t*>(x);
-  if (kind == 0)
-    hipLaunchKernelGGL((act_quant_kernel<128, 0, kActUnroll, 1>), grid, dim3(256), 0, s, xp, K, K, q, K, scales);
-  else
-    hipLaunchKernelGGL((act_quant_kernel<128, 0, kActUnroll, 2>), grid, dim3(256), 0, s, xp, K, K, q, K, scales);
   return check_launch();
 }
 

@@ -436,11 +436,12 @@ int fp8b_mfma_loop(int kind, const uint32_t *ops, int64_t iters, int64_t workgro
                    float *out, void *stream);
 
 /*
- * fp8b_stream_probe -- a measurement aid, not a step of the method: the
- * launch of fp8_act_quant (block 128, fp32 scales) on x bf16 [M][K]
- * (contiguous rows) with the same grid, loads and stores, but
- *   FP8B_PROBE_COPY:  no arithmetic -- q[m][k] = low byte of x[m][k] and
- *                     scales[m][k/128] = 0 (the same bytes moved);
+ * fp8b_stream_probe -- a measurement aid, not a step of the method: two
+ * kernels of their own with the grid and workgroup shape of fp8_act_quant
+ * (block 128, fp32 scales) on x bf16 [M][K] (contiguous rows):
+ *   FP8B_PROBE_COPY:  act_quant's loads and stores without its arithmetic --
+ *                     q[m][k] = low byte of x[m][k] and scales[m][k/128] = 0
+ *                     (the same bytes moved);
  *   FP8B_PROBE_EMPTY: every workgroup returns at once (launch and drain).
  * Timed beside fp8_act_quant it separates the memory system's rate for this
  * access pattern, and the launch's fixed cost, from the quantiser's own work.

@@ -656,13 +656,15 @@ def test_gemms_with_activations_beyond_4gib(F, orc):
 
 # ---- 1 .. 64 tokens on packed weights (weights streamed into registers) ----
 @pytest.mark.parametrize("N,K", [(128, 256), (384, 512), (256, 768), (640, 1024), (128, 1280),
-                                 (256, 1536), (384, 1792), (128, 2048), (256, 2560)])
+                                 (256, 1536), (384, 1792), (128, 2048), (256, 2560),
+                                 (896, 768), (1792, 1024), (896, 2560)])
 def test_block_gemm_register_streamed_decode(F, orc, N, K):
     """Packed weights with at most 64 tokens, a grid of at most one 128-row
-    tile per CU and an even K-block count: one to eight and ten steps per
-    K-split group (a main loop of three and a tail of one to four steps),
-    one and two 32-token fragments with ragged last fragments, both scale
-    formats and output types; every output against the oracle."""
+    tile per CU and an even K-block count: one to eight and ten steps per K-split
+    group (a main loop of three and a tail of one to four steps), one and
+    two 32-token fragments with ragged last fragments, both scale formats
+    and output types, grids of one to fourteen tiles; every output against
+    the oracle."""
     c = W.decode_linear(K=K, N=N, seed=N + K)
     for fmt, out in (("ue8m0", torch.bfloat16), ("fp32", torch.float32)):
         fi = {"fp32": 0, "ue8m0": 1}[fmt]
