@@ -698,3 +698,30 @@ def test_register_streamed_decode_rows_equal_the_tiled_kernel(F, N, K):
             torch.cuda.synchronize()
             iv = torch.int16 if out == torch.bfloat16 else torch.int32
             assert torch.equal(y.view(iv), ref[:M].view(iv)), f"M {M} {out} {N}x{K}"
+
+
+@pytest.mark.parametrize("M", [5, 30, 33, 64])
+def test_register_streamed_decode_strided_operands(F, orc, M):
+    """The register-streamed kernel on activation rows with a leading
+    dimension above K (a column slice of a wider code matrix, whose bytes
+    past K hold codes that must never be read) and an output that is a
+    column slice of a wider y (bytes past N must stay untouched)."""
+    N, K, extra = 384, 1024, 128
+    c = W.decode_linear(K=K, N=N, seed=13 * M)
+    a, sa = F.fp8_act_quant(c.x[:M].to(DEV), 128, "ue8m0")
+    wq, ws = F.fp8_weight_quant(c.w.to(DEV), "ue8m0")
+    wp = F.fp8_weight_pack(wq)
+    wide = torch.full((M, K + extra), 0x7E, dtype=torch.uint8, device=DEV)
+    wide[:, :K] = a
+    ywide = torch.full((M, N + 64), -7.0, dtype=torch.bfloat16, device=DEV)
+    y = F.fp8_block_gemm_packed(wide[:, :K], sa, wp, ws, torch.bfloat16, y=ywide[:, :N])
+    torch.cuda.synchronize()
+    assert y.stride(0) == N + 64
+    assert torch.all(ywide[:, N:] == -7.0), "bytes past N written"
+    oa, osa = orc.act_quant(W.bits(c.x[:M]), 128, 1)
+    ow, osw = orc.weight_quant(W.bits(c.w), 1)
+    yr, bnd = orc.block_gemm(oa, osa, ow, osw)
+    assert_parity(_np(ywide[:, :N]), yr, bnd, True, f"strided M {M}")
+    dense = F.fp8_block_gemm_packed(a, sa, wp, ws, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(dense.view(torch.int16), ywide[:, :N].contiguous().view(torch.int16)), f"strided vs dense M {M}"
