@@ -725,3 +725,25 @@ def test_register_streamed_decode_strided_operands(F, orc, M):
     dense = F.fp8_block_gemm_packed(a, sa, wp, ws, torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(dense.view(torch.int16), ywide[:, :N].contiguous().view(torch.int16)), f"strided vs dense M {M}"
+
+
+@pytest.mark.parametrize("extra_tiles", [0, 1])
+def test_register_streamed_decode_at_the_cu_count(F, orc, extra_tiles):
+    """Packed weights with N / 128 equal to the CU count take the
+    register-streamed kernel (one tile per CU); one tile more and the GEMM
+    falls back to the streaming kernel.  Both sides against the oracle on
+    sampled token rows x every column, 1 and 40 tokens."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N, K = 128 * (cus + extra_tiles), 256
+    c = W.decode_linear(K=K, N=N, seed=17 + extra_tiles)
+    a, sa = F.fp8_act_quant(c.x[:40].to(DEV), 128, "ue8m0")
+    wq, ws = F.fp8_weight_quant(c.w.to(DEV), "ue8m0")
+    wp = F.fp8_weight_pack(wq)
+    ow, osw = orc.weight_quant(W.bits(c.w), 1)
+    for M in (1, 40):
+        y = F.fp8_block_gemm_packed(a[:M], sa[:M], wp, ws, torch.bfloat16)
+        torch.cuda.synchronize()
+        rows = sorted({0, M - 1})
+        oa, osa = orc.act_quant(W.bits(c.x[rows]), 128, 1)
+        yr, bnd = orc.block_gemm(oa, osa, ow, osw)
+        assert_parity(_np(y[rows]), yr, bnd, True, f"M {M} N {N}")
