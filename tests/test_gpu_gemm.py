@@ -115,13 +115,14 @@ def test_block_gemm_scale_products_near_the_fp32_range_ends(F, orc, M, K, scale,
         assert_parity(_np(y), yr, bnd, out == torch.bfloat16, f"scale products {scale}, M {M}")
 
 
-@pytest.mark.parametrize("M", [40, 300])
-def test_linear_step_graph_replay_matches_eager(F, M):
+@pytest.mark.parametrize("M,K", [(40, 640), (300, 640), (8, 1024), (40, 1024)])
+def test_linear_step_graph_replay_matches_eager(F, M, K):
     """act_quant + block GEMM (packed weights) captured once as a HIP graph
     and replayed on new activations, with eager work between replays: every
     replay equals the eager step bit for bit (no allocation, memset or
-    synchronisation is recorded)."""
-    N, K = 384, 640
+    synchronisation is recorded).  K 640 (five K blocks) takes the streaming
+    kernel and the tiles, K 1024 the register-streamed kernel."""
+    N = 384
     g = torch.Generator(device=DEV).manual_seed(61 + M)
     w = (torch.randn(N, K, device=DEV, generator=g) * 0.02).to(torch.bfloat16)
     wq, ws = F.fp8_weight_quant(w, "fp32")
