@@ -84,6 +84,8 @@ def lib():
         L.fp8_delayed_state_init.argtypes = [vp, i64, vp]
         L.fp8_delayed_quant.restype = ci
         L.fp8_delayed_quant.argtypes = [vp, i64, vp, i64, ci, ctypes.c_float, vp, vp, vp]
+        L.fp8_delayed_quant_noalloc.restype = ci
+        L.fp8_delayed_quant_noalloc.argtypes = [vp, i64, vp, i64, ci, ctypes.c_float, vp, vp, vp]
         L.fp8_cast_f32.restype = ci
         L.fp8_cast_f32.argtypes = [vp, i64, ci, vp, vp]
         L.fp8b_stream_probe.restype = ci
@@ -305,6 +307,20 @@ class DelayedScaler:
         rc = lib().fp8_delayed_quant(_p(x), x.numel(), _p(self.state), self.history_len, self.algo,
                                      self.divisor, _p(q), _p(scale_used), _stream(x))
         _check("fp8_delayed_quant", rc)
+        return q, scale_used
+
+    def quantize_noalloc(self, x: torch.Tensor, q: torch.Tensor, scale_used: torch.Tensor):
+        """The same step through fp8_delayed_quant_noalloc: the caller
+        passes the outputs, and the library's static per-GPU scratch holds
+        the step in flight (steps on one GPU must not overlap)."""
+        _need(x.dtype == torch.bfloat16 and x.is_contiguous(), "x must be contiguous bf16")
+        _need(q.dtype == torch.uint8 and q.is_contiguous() and q.numel() == x.numel(),
+              "q must be contiguous uint8 with one code per element of x")
+        _need(scale_used.dtype == torch.float32 and scale_used.numel() >= 1, "scale_used must be float32 [1]")
+        _on_gpu(x, self.state, q, scale_used)
+        rc = lib().fp8_delayed_quant_noalloc(_p(x), x.numel(), _p(self.state), self.history_len, self.algo,
+                                             self.divisor, _p(q), _p(scale_used), _stream(x))
+        _check("fp8_delayed_quant_noalloc", rc)
         return q, scale_used
 
 

@@ -36,6 +36,18 @@ int grouped_check(const uint8_t* a, const float* a_scales, int64_t T, const int3
   return FP8B_OK;
 }
 
+// Arguments shared by the delayed-scaling steps.
+int delayed_check(const void* x, int64_t n, const void* state, int64_t history_len, int algo, float amax_divisor,
+                  const uint8_t* q, const float* scale_used) {
+  if (algo != FP8B_AMAX_MAX && algo != FP8B_AMAX_LATEST) return FP8B_EUNSUPPORTED;
+  if (!x || !state || !q || !scale_used) return FP8B_EINVAL;
+  if (n <= 0 || n % 8 != 0 || n / 8 / 1024 >= INT32_MAX) return FP8B_EINVAL;
+  if (history_len < 1 || history_len > FP8B_DELAYED_MAX_HISTORY) return FP8B_EINVAL;
+  if (!(amax_divisor > 0.0f) || amax_divisor > 3.0e38f) return FP8B_EINVAL;
+  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(state, 16) || !aligned(scale_used, 4)) return FP8B_EALIGN;
+  return FP8B_OK;
+}
+
 }  // namespace
 
 #define FP8B_EXPORT __attribute__((visibility("default")))
@@ -212,14 +224,18 @@ FP8B_EXPORT int fp8_delayed_state_init(void* state, int64_t history_len, void* s
 
 FP8B_EXPORT int fp8_delayed_quant(const void* x, int64_t n, void* state, int64_t history_len, int algo,
                                   float amax_divisor, uint8_t* q, float* scale_used, void* stream) {
-  if (algo != FP8B_AMAX_MAX && algo != FP8B_AMAX_LATEST) return FP8B_EUNSUPPORTED;
-  if (!x || !state || !q || !scale_used) return FP8B_EINVAL;
-  if (n <= 0 || n % 8 != 0 || n / 8 / 1024 >= INT32_MAX) return FP8B_EINVAL;
-  if (history_len < 1 || history_len > FP8B_DELAYED_MAX_HISTORY) return FP8B_EINVAL;
-  if (!(amax_divisor > 0.0f) || amax_divisor > 3.0e38f) return FP8B_EINVAL;
-  if (!aligned(x, 16) || !aligned(q, 8) || !aligned(state, 16) || !aligned(scale_used, 4)) return FP8B_EALIGN;
+  const int rc = delayed_check(x, n, state, history_len, algo, amax_divisor, q, scale_used);
+  if (rc != FP8B_OK) return rc;
   return fp8blk::launch_delayed_quant(x, n, state, history_len, algo, amax_divisor, q, scale_used,
                                       as_stream(stream));
+}
+
+FP8B_EXPORT int fp8_delayed_quant_noalloc(const void* x, int64_t n, void* state, int64_t history_len, int algo,
+                                          float amax_divisor, uint8_t* q, float* scale_used, void* stream) {
+  const int rc = delayed_check(x, n, state, history_len, algo, amax_divisor, q, scale_used);
+  if (rc != FP8B_OK) return rc;
+  return fp8blk::launch_delayed_quant_noalloc(x, n, state, history_len, algo, amax_divisor, q, scale_used,
+                                              as_stream(stream));
 }
 
 FP8B_EXPORT int fp8_cast_f32(const float* x, int64_t n, int fmt, uint8_t* q, void* stream) {

@@ -27,6 +27,8 @@ int launch_moe_combine(const void* y, int64_t R, int64_t N, const int32_t* token
 int launch_delayed_init(void* state, int64_t L, hipStream_t s);
 int launch_delayed_quant(const void* x, int64_t n, void* state, int64_t L, int algo, float divisor, uint8_t* q,
                          float* scale_used, hipStream_t s);
+int launch_delayed_quant_noalloc(const void* x, int64_t n, void* state, int64_t L, int algo, float divisor,
+                                 uint8_t* q, float* scale_used, hipStream_t s);
 int launch_weight_dequant(const uint8_t* q, int64_t N, int64_t K, int64_t ldq, const float* scales,
                           void* w, int64_t ldw, hipStream_t s);
 int launch_weight_pack(const uint8_t* w, int64_t G, int64_t N, int64_t K, int64_t ldw, uint8_t* out,

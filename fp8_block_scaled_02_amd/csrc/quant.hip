@@ -12,6 +12,7 @@
 // no barrier), and each lane writes its 8 codes with one 8-byte
 // non-temporal store.
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -300,10 +301,13 @@ __global__ __launch_bounds__(256) void delayed_init_kernel(uint8_t* __restrict__
 // One step: codes = E4M3(clamp(x / d, +-448)) with the stored scale d
 // (IEEE division: d comes from another tensor, so the quotient can take any
 // magnitude), one chunk of 8192 values per workgroup.  Each workgroup folds
-// its amax into one of the state's 16 amax slots (workgroup b into slot
-// b mod 16) with an atomic max (non-negative floats order like their bit
-// patterns), then takes a ticket of its slot; the workgroup completing a
-// slot takes a ticket of the step, and the one completing the step has
+// its amax into one of 16 amax slots (workgroup b into slot b mod 16; the
+// 128-byte line at slots + 32 b holds the slot's maximum in word 0 and its
+// ticket in word 1: the state's slots, or the library's static scratch for
+// fp8_delayed_quant_noalloc) with an atomic max (non-negative floats order
+// like their bit patterns), then takes a ticket of its slot; the workgroup
+// completing a slot takes a ticket of the step (*done), and the one
+// completing the step has
 // every workgroup's maximum in the slots (each one's atomic max completed
 // before its tickets).  Spreading the atomics over 16 lines keeps them from
 // queueing on one word.  That workgroup closes the step: it merges and
@@ -314,8 +318,8 @@ __global__ __launch_bounds__(256) void delayed_init_kernel(uint8_t* __restrict__
 constexpr int kDelayedUnroll = 4;
 
 __global__ __launch_bounds__(256) void delayed_step_kernel(
-    const uint16_t* __restrict__ x, int64_t n, uint8_t* __restrict__ st, int L, int algo, float divisor,
-    uint8_t* __restrict__ q, float* __restrict__ scale_used) {
+    const uint16_t* __restrict__ x, int64_t n, uint8_t* __restrict__ st, uint32_t* slots, uint32_t* done, int L,
+    int algo, float divisor, uint8_t* __restrict__ q, float* __restrict__ scale_used) {
   DelayedHeader* hd = reinterpret_cast<DelayedHeader*>(st);
   float* hist = reinterpret_cast<float*>(st + sizeof(DelayedHeader));
   __shared__ float red[4];
@@ -371,7 +375,7 @@ __global__ __launch_bounds__(256) void delayed_step_kernel(
     // device-scope atomics, performed where every XCD sees them, so no
     // fence is needed: the closing workgroup reads nothing else.
     const int sl = (int)(blockIdx.x % FP8B_DELAYED_AMAX_SLOTS);
-    uint32_t* line = &hd->amax[sl][0];
+    uint32_t* line = slots + 32 * sl;
     const uint32_t prev = __hip_atomic_fetch_max(line, __float_as_uint(amax), __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("" ::"v"(prev) : "memory");
@@ -379,8 +383,8 @@ __global__ __launch_bounds__(256) void delayed_step_kernel(
     const uint32_t t = __hip_atomic_fetch_add(line + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (t == in_slot - 1) {  // this slot is complete
       asm volatile("" ::"v"(t) : "memory");
-      const uint32_t slots = min(gridDim.x, (unsigned)FP8B_DELAYED_AMAX_SLOTS);
-      closer = __hip_atomic_fetch_add(&hd->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == slots - 1;
+      const uint32_t nslots = min(gridDim.x, (unsigned)FP8B_DELAYED_AMAX_SLOTS);
+      closer = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nslots - 1;
     }
   }
   if (!__shfl(closer, 0)) return;
@@ -389,9 +393,9 @@ __global__ __launch_bounds__(256) void delayed_step_kernel(
   const int lane = tid;
   uint32_t ab = 0u;
   if (lane < FP8B_DELAYED_AMAX_SLOTS) {
-    ab = __hip_atomic_load(&hd->amax[lane][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&hd->amax[lane][0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&hd->amax[lane][1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ab = __hip_atomic_load(slots + 32 * lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(slots + 32 * lane, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(slots + 32 * lane + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   float a = __uint_as_float(ab);
   a = row16_max(a);
@@ -411,7 +415,7 @@ __global__ __launch_bounds__(256) void delayed_step_kernel(
     hd->pos = (pos + 1) % L;
     hd->filled = filled;
     hd->scale = (h == 0.0f) ? 1.0f : h / divisor;
-    __hip_atomic_store(&hd->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -578,13 +582,77 @@ int launch_delayed_init(void* state, int64_t L, hipStream_t s) {
   return check_launch();
 }
 
-int launch_delayed_quant(const void* x, int64_t n, void* state, int64_t L, int algo, float divisor, uint8_t* q,
-                         float* scale_used, hipStream_t s) {
+static int delayed_step(const void* x, int64_t n, void* state, uint32_t* slots, uint32_t* done, int64_t L,
+                        int algo, float divisor, uint8_t* q, float* scale_used, hipStream_t s) {
   const int64_t per_wg = 256 * kDelayedUnroll;
   const dim3 grid((unsigned)((n / 8 + per_wg - 1) / per_wg));
   hipLaunchKernelGGL(delayed_step_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(x), n,
-                     static_cast<uint8_t*>(state), (int)L, algo, divisor, q, scale_used);
+                     static_cast<uint8_t*>(state), slots, done, (int)L, algo, divisor, q, scale_used);
   return check_launch();
+}
+
+int launch_delayed_quant(const void* x, int64_t n, void* state, int64_t L, int algo, float divisor, uint8_t* q,
+                         float* scale_used, hipStream_t s) {
+  DelayedHeader* h = static_cast<DelayedHeader*>(state);
+  return delayed_step(x, n, state, &h->amax[0][0], &h->done, L, algo, divisor, q, scale_used, s);
+}
+
+// ---- delayed scaling without a caller-provided scratch -------------------------
+// fp8_delayed_quant_noalloc keeps the step-in-flight scratch (the 16 amax
+// slot lines and the step ticket, one 128-byte line each) in this array
+// instead of the state.  Every GPU holds its own copy at its own address
+// until the process ends.  In host code `scratch` is only a stand-in for
+// the symbol: its device address is looked up once per device and kept in
+// scratch_dev, and only that address is passed to kernels.
+constexpr int kDelayedScratchWords = (FP8B_DELAYED_AMAX_SLOTS + 1) * 32;
+static_assert(kDelayedScratchWords * 4 == FP8B_DELAYED_NOALLOC_SCRATCH_BYTES, "scratch size in the header");
+static __device__ __align__(256) uint32_t scratch[kDelayedScratchWords];
+
+__global__ __launch_bounds__(256) void scratch_clear_kernel(uint32_t* __restrict__ p, int words) {
+  for (int i = threadIdx.x; i < words; i += 256) p[i] = 0u;
+}
+
+constexpr int kMaxScratchDevices = 64;
+static uint32_t* scratch_dev[kMaxScratchDevices];  // device address of `scratch`, per device
+static std::mutex scratch_mu;
+
+// Device address of this stream's device's scratch.  The first call on a
+// device looks the address up with that device current and clears the
+// array with a kernel on the caller's stream (ordered before the step that
+// follows; later steps leave it cleared: the closing workgroup zeroes the
+// slots and the ticket).
+static int delayed_scratch(hipStream_t s, uint32_t** out) {
+  hipDevice_t dev = 0;
+  if (s == nullptr || hipStreamGetDevice(s, &dev) != hipSuccess) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return FP8B_ELAUNCH;
+    dev = cur;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return FP8B_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_dev[dev] == nullptr) {
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess) return FP8B_ELAUNCH;
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) return FP8B_ELAUNCH;
+    void* p = nullptr;
+    const hipError_t rc = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (prev != dev) (void)hipSetDevice(prev);
+    if (rc != hipSuccess || p == nullptr) return FP8B_ELAUNCH;
+    hipLaunchKernelGGL(scratch_clear_kernel, dim3(1), dim3(256), 0, s, static_cast<uint32_t*>(p),
+                       kDelayedScratchWords);
+    if (check_launch() != FP8B_OK) return FP8B_ELAUNCH;
+    scratch_dev[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = scratch_dev[dev];
+  return FP8B_OK;
+}
+
+int launch_delayed_quant_noalloc(const void* x, int64_t n, void* state, int64_t L, int algo, float divisor,
+                                 uint8_t* q, float* scale_used, hipStream_t s) {
+  uint32_t* p = nullptr;
+  const int rc = delayed_scratch(s, &p);
+  if (rc != FP8B_OK) return rc;
+  return delayed_step(x, n, state, p, p + FP8B_DELAYED_AMAX_SLOTS * 32, L, algo, divisor, q, scale_used, s);
 }
 
 int launch_cast(const float* x, int64_t n, int fmt, uint8_t* q, hipStream_t s) {

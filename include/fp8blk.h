@@ -37,7 +37,9 @@
  *    rounded to nearest, ties to even.  A negative value that rounds to
  *    zero gives code 0x80.
  *  - Non-finite inputs give unspecified codes/outputs but never fault.
- *  - Thread-safe; no global mutable state.
+ *  - Thread-safe.  Global state: the compute-unit count of each device,
+ *    queried once and cached, and the static device scratch of
+ *    fp8_delayed_quant_noalloc (see there).
  */
 #ifndef FP8BLK_H
 #define FP8BLK_H
@@ -392,6 +394,35 @@ int fp8_delayed_state_init(void *state, int64_t history_len, void *stream);
 int fp8_delayed_quant(const void *x, int64_t n, void *state,
                       int64_t history_len, int algo, float amax_divisor,
                       uint8_t *q, float *scale_used, void *stream);
+
+/*
+ * fp8_delayed_quant_noalloc -- for callers that cannot allocate device
+ * memory or bring a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): fp8_delayed_quant with the
+ * step-in-flight scratch (the amax slots and the step ticket) kept in a
+ * file-scope static device array of the library instead of the state.
+ * Same arguments, checks, results and state layout as fp8_delayed_quant;
+ * the state's step_amax lines and `done` word are left untouched, and a
+ * state may be advanced by either entry point.
+ *
+ *   The scratch is FP8B_DELAYED_NOALLOC_SCRATCH_BYTES (2176) bytes per GPU,
+ *   whatever n is, held from the first call on that GPU until the process
+ *   ends.  n is bounded as for fp8_delayed_quant (n % 8 == 0,
+ *   n / 8192 < 2^31): larger sizes return FP8B_EINVAL.
+ *   The first call on a GPU looks up the array's device address (with that
+ *   GPU current) and clears it with a kernel on `stream`; each step leaves
+ *   it cleared for the next.  No hipMalloc/hipFree or other allocation.
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap on
+ *   one GPU (on different streams, or in one graph without an order
+ *   between them) race and give wrong scales.  Order them.
+ *   Returns FP8B_ELAUNCH if the symbol lookup or a launch fails, and
+ *   FP8B_EUNSUPPORTED on a device index of 64 or more.
+ */
+#define FP8B_DELAYED_NOALLOC_SCRATCH_BYTES (128 * (FP8B_DELAYED_AMAX_SLOTS + 1))
+int fp8_delayed_quant_noalloc(const void *x, int64_t n, void *state,
+                              int64_t history_len, int algo,
+                              float amax_divisor, uint8_t *q,
+                              float *scale_used, void *stream);
 
 /*
  * fp8_cast_f32 -- FP8Cast of "量化: FP8 与混合精度推理" (x_fp8 =

@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
     assert _declared() == sorted([
         "fp8b_abi_version", "fp8b_status_string", "fp8_act_quant", "fp8_weight_quant",
         "fp8_block_gemm", "mxfp8_gemm", "fp8_grouped_gemm", "fp8_moe_combine", "fp8_weight_dequant", "fp8_kv_quant", "fp8_kv_dequant",
-        "fp8_delayed_state_init", "fp8_delayed_quant", "fp8_cast_f32",
+        "fp8_delayed_state_init", "fp8_delayed_quant", "fp8_delayed_quant_noalloc", "fp8_cast_f32",
         "fp8_weight_pack", "fp8_block_gemm_packed", "fp8_grouped_gemm_packed", "fp8b_mfma_loop",
         "fp8b_stream_probe"])
 
@@ -103,9 +103,12 @@ def test_moe_combine_validation(L):
     assert f(*bad) == 0                                                   # T = 0
 
 
-def test_delayed_validation(L):
-    f = L.fp8_delayed_quant
+@pytest.mark.parametrize("name", ["fp8_delayed_quant", "fp8_delayed_quant_noalloc"])
+def test_delayed_validation(L, name):
+    f = getattr(L, name)
     args = [GOOD, 1024, GOOD, 16, 0, 400.0, GOOD, GOOD, NULL]
+    bad = list(args); bad[1] = (1 << 31) * 8192
+    assert f(*bad) == -1                                                  # n beyond the bound
     bad = list(args); bad[4] = 2
     assert f(*bad) == -3
     bad = list(args); bad[1] = 100
