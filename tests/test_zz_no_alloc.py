@@ -110,3 +110,39 @@ def test_noalloc_rejects_what_delayed_quant_rejects(F):
     assert f(_ptr(x), (1 << 31) * 8192, _ptr(st), 4, 0, ctypes.c_float(400.0), _ptr(q), _ptr(su), _stream()) == -1
     assert f(_ptr(x), 64, _ptr(st), 4, 2, ctypes.c_float(400.0), _ptr(q), _ptr(su), _stream()) == -3
     torch.cuda.synchronize()
+
+
+def test_noalloc_step_replays_from_a_graph(F, orc):
+    """The use the entry point is for: a step captured in a HIP graph (no
+    allocation inside the capture) and replayed on new inputs, with eager
+    work and synchronisations between the replays, follows the oracle's
+    scale sequence; the state is advanced only by the replays."""
+    L, S, n = 4, 5, 8192 * 9 + 64
+    g = W.gen(2024, DEV)
+    mag = torch.exp2(torch.tensor([3.0, -2.0, 5.0, 0.0, -6.0], device=DEV)).reshape(S, 1)
+    x = (torch.randn(S, n, generator=g, device=DEV) * mag).to(torch.bfloat16)
+    ds = F.DelayedScaler(L, "max", 400.0)
+    buf = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    q = torch.empty(n, dtype=torch.uint8, device=DEV)
+    su = torch.empty(1, dtype=torch.float32, device=DEV)
+    buf.copy_(x[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):       # an eager step first (the library's set-up on this GPU)
+        ds.quantize_noalloc(buf, q, su)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ds.reset()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ds.quantize_noalloc(buf, q, su)
+    ds.reset()                          # capture does not run the step
+    q2, s2 = orc.delayed_scaling(W.bits(x.cpu()), L, 0, 400.0)
+    for s in range(S):
+        buf.copy_(x[s])
+        graph.replay()
+        torch.cuda.synchronize()
+        assert su.item() == s2[s], s
+        assert (q.cpu().numpy() == q2[s]).all(), s
+        _ = (x[s].float() * 2).sum().item()   # eager work between replays
