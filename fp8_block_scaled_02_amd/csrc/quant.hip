@@ -635,12 +635,14 @@ static int delayed_scratch(hipStream_t s, uint32_t** out) {
     if (hipGetDevice(&prev) != hipSuccess) return FP8B_ELAUNCH;
     if (prev != dev && hipSetDevice(dev) != hipSuccess) return FP8B_ELAUNCH;
     void* p = nullptr;
-    const hipError_t rc = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    int rc = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p != nullptr ? FP8B_OK : FP8B_ELAUNCH;
+    if (rc == FP8B_OK) {  // cleared on the caller's stream, with its device still current
+      hipLaunchKernelGGL(scratch_clear_kernel, dim3(1), dim3(256), 0, s, static_cast<uint32_t*>(p),
+                         kDelayedScratchWords);
+      rc = check_launch();
+    }
     if (prev != dev) (void)hipSetDevice(prev);
-    if (rc != hipSuccess || p == nullptr) return FP8B_ELAUNCH;
-    hipLaunchKernelGGL(scratch_clear_kernel, dim3(1), dim3(256), 0, s, static_cast<uint32_t*>(p),
-                       kDelayedScratchWords);
-    if (check_launch() != FP8B_OK) return FP8B_ELAUNCH;
+    if (rc != FP8B_OK) return FP8B_ELAUNCH;
     scratch_dev[dev] = static_cast<uint32_t*>(p);
   }
   *out = scratch_dev[dev];
