@@ -139,6 +139,25 @@ def timed(torch, fn, iters, warm_ms=100.0):
     return e0.elapsed_time(e1) / iters * 1e-3
 
 
+def interleaved(torch, fns, rounds=4, iters=10):
+    """Median per-launch device time of each fn over `rounds` alternating
+    rounds of `iters` launches (A B A B ...), after a shared warm-up: the
+    kernels compared see the same clock state."""
+    warm(torch, lambda: [f() for f in fns], 100.0)
+    s = torch.cuda.current_stream()
+    times = [[] for _ in fns]
+    for _ in range(rounds):
+        for i, f in enumerate(fns):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for _ in range(iters):
+                f()
+            e1.record(s)
+            e1.synchronize()
+            times[i].append(e0.elapsed_time(e1) / iters * 1e-3)
+    return [statistics.median(t) for t in times]
+
+
 def timed_graph(torch, fn, iters):
     """Average device time of fn() for kernels short enough that host-side
     argument marshalling between launches would leave the GPU idle: iters
@@ -270,6 +289,13 @@ def main():
     t_copy = timed_graph(torch, lambda: F.fp8b_stream_probe(F.PROBE_COPY, x, a, sa), max(args.steps, 10))
     t_empty = timed_graph(torch, lambda: F.fp8b_stream_probe(F.PROBE_EMPTY, x, a, sa), max(args.steps, 10))
     aq()                                   # restore the step's codes and scales
+    # the same GEMM kernel with every tile reading tile (0, 0)'s operands
+    # (fp8b_gemm_probe: the same work, operands resident in L2), interleaved
+    # with the GEMM itself: what the operand traffic beyond L2 costs
+    y_probe = torch.empty_like(y)
+    t_g2, t_probe = interleaved(torch, [gemm, lambda: F.fp8b_gemm_probe(F.GEMM_PROBE_TILE0, a, sa, wq, ws,
+                                                                         y=y_probe)])
+    del y_probe
     gemm_bytes = M * K + N * K + M * (K // 128) * 4 + (N // 128) * (K // 128) * 4 + M * N * 2
     aq_bytes = M * K * 2 + M * K + M * (K // 128) * 4
     achieved = flops / t_gemm / 1e12
@@ -291,6 +317,11 @@ def main():
                                            "note": "same grid, loads and stores as act_quant: copy moves the "
                                                    "same bytes with no arithmetic, empty returns at once"},
                        "gemm_us": round(t_gemm * 1e6, 2), "gemm_TFLOPs": round(achieved, 1),
+                       "gemm_l2_probe": {"gemm_us": round(t_g2 * 1e6, 2), "probe_us": round(t_probe * 1e6, 2),
+                                         "probe_vs_gemm": round(t_probe / t_g2, 4),
+                                         "note": "interleaved medians: the GEMM, and the same kernel with every "
+                                                 "tile reading tile (0, 0)'s operands (no operand traffic "
+                                                 "beyond L2)"},
                        "weights": "packed layout (fp8_weight_pack, offline)"}
     del c
 

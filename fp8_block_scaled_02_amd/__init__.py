@@ -26,6 +26,7 @@ OUT_F32, OUT_BF16 = 0, 1
 FMT_E4M3, FMT_E5M2 = 0, 1
 MFMA_BF16_16X16X32, MFMA_FP8_16X16X128 = 0, 1
 PROBE_COPY, PROBE_EMPTY = 0, 1
+GEMM_PROBE_TILE0 = 0
 MFMA_LOOP_FLOPS = {MFMA_BF16_16X16X32: 16384, MFMA_FP8_16X16X128: 65536}   # per MFMA instruction
 DELAYED_HEADER_BYTES = 128 + 128 * 16    # FP8B_DELAYED_HEADER_BYTES of include/fp8blk.h
 
@@ -90,6 +91,8 @@ def lib():
         L.fp8_cast_f32.argtypes = [vp, i64, ci, vp, vp]
         L.fp8b_stream_probe.restype = ci
         L.fp8b_stream_probe.argtypes = [ci, vp, i64, i64, vp, vp, vp]
+        L.fp8b_gemm_probe.restype = ci
+        L.fp8b_gemm_probe.argtypes = [ci, vp, vp, vp, vp, i64, i64, i64, vp, vp]
         L.fp8b_mfma_loop.restype = ci
         L.fp8b_mfma_loop.argtypes = [ci, vp, i64, i64, vp, vp]
         _lib = L
@@ -422,6 +425,27 @@ def fp8_block_gemm_packed(a, a_scales, w_packed, w_scales, out_dtype=torch.bfloa
     rc = lib().fp8_block_gemm_packed(_p(a), a.stride(0) if M else K, _p(a_scales), _p(w_packed), _p(w_scales),
                                      M, N, K, _p(y), y.stride(0) if M else N, od, _stream(a))
     _check("fp8_block_gemm_packed", rc)
+    return y
+
+
+def fp8b_gemm_probe(kind: int, a, a_scales, w_packed, w_scales, y=None):
+    """The prefill block GEMM kernel with every tile reading tile (0, 0)'s
+    operands (a measurement aid, not a step of the method): the same work as
+    fp8_block_gemm_packed with bf16 output, no operand traffic beyond L2.
+    a [M, K] contiguous, w_packed [N, K]; M, N, K multiples of 128."""
+    _need(w_packed.dim() == 2 and w_packed.is_contiguous(), "w_packed must be a contiguous [N, K] tensor")
+    _gemm_operands(a, a_scales, w_packed, w_scales)
+    _need(a.is_contiguous(), "a must be contiguous")
+    M, K = a.shape
+    N = w_packed.shape[0]
+    if y is None:
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=a.device)
+    _gemm_output(y, M, N, torch.bfloat16)
+    _need(y.is_contiguous(), "y must be contiguous")
+    _on_gpu(a, a_scales, w_packed, w_scales, y)
+    rc = lib().fp8b_gemm_probe(int(kind), _p(a), _p(a_scales), _p(w_packed), _p(w_scales), M, N, K, _p(y),
+                               _stream(a))
+    _check("fp8b_gemm_probe", rc)
     return y
 
 

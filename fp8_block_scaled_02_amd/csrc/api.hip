@@ -257,6 +257,19 @@ FP8B_EXPORT int fp8b_stream_probe(int kind, const void* x, int64_t M, int64_t K,
   return fp8blk::launch_stream_probe(kind, x, M, K, q, scales, as_stream(stream));
 }
 
+FP8B_EXPORT int fp8b_gemm_probe(int kind, const uint8_t* a, const float* a_scales, const uint8_t* w_packed,
+                                const float* w_scales, int64_t M, int64_t N, int64_t K, void* y, void* stream) {
+  if (kind != FP8B_GEMM_PROBE_TILE0) return FP8B_EUNSUPPORTED;
+  if (!a || !a_scales || !w_packed || !w_scales || !y) return FP8B_EINVAL;
+  if (M < 128 || N < 128 || K < 128 || M % 128 != 0 || N % 128 != 0 || K % 128 != 0) return FP8B_EINVAL;
+  if (M > kMaxDim || N > kMaxPackedN || K >= kMaxLd || N >= kMaxLd) return FP8B_EINVAL;
+  if ((M / 128) * (N / 128) >= INT32_MAX) return FP8B_EINVAL;
+  if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(y, 16) || !aligned(a_scales, 4) ||
+      !aligned(w_scales, 4))
+    return FP8B_EALIGN;
+  return fp8blk::launch_gemm_probe(a, a_scales, w_packed, w_scales, M, N, K, y, as_stream(stream));
+}
+
 FP8B_EXPORT int fp8b_mfma_loop(int kind, const uint32_t* ops, int64_t iters, int64_t workgroups, float* out,
                                void* stream) {
   if (kind != FP8B_MFMA_BF16_16X16X32 && kind != FP8B_MFMA_FP8_16X16X128) return FP8B_EUNSUPPORTED;

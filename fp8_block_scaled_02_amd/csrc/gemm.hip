@@ -802,7 +802,12 @@ __device__ __forceinline__ void ksplit_sum(uint8_t* lds, Acc32<C>& acc) {
   }
 }
 
-template <class C, bool BF16, bool PK, bool M32 = false>
+// TILE0 is a measurement aid (fp8b_gemm_probe), not a step of the method:
+// every workgroup reads the operands and scales of output tile (0, 0) --
+// which then stay resident in L2 -- and stores its results to its own tile,
+// so the launch does the same work as the GEMM with no operand traffic
+// beyond L2.
+template <class C, bool BF16, bool PK, bool M32 = false, bool TILE0 = false>
 __global__ __launch_bounds__(C::NT, 512 / C::NT) void block_gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ SA,
     const uint8_t* __restrict__ W, int64_t ldw, const float* __restrict__ SW, int M, int N, int K,
@@ -812,7 +817,8 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void block_gemm_kernel(
   const int tiles_m = (M + C::BM - 1) / C::BM, tiles_n = N / C::BN;
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int m0 = tm * C::BM, n0 = tn * C::BN;         // output tile
+  const int om0 = TILE0 ? 0 : m0, on0 = TILE0 ? 0 : n0;  // operand tile
   const int lane = threadIdx.x & 63, wave = wave_of<C>();
   const int group = C::KS > 1 ? wave_id() / C::NW : 0;  // this group's first K block
   const int nkb = K / kBK, nkb_g = nkb / C::KS;          // the launcher keeps nkb % KS == 0
@@ -821,27 +827,27 @@ __global__ __launch_bounds__(C::NT, 512 / C::NT) void block_gemm_kernel(
   // 64-bit tile bases, 32-bit per-lane offsets inside the tile (the entry
   // point keeps every leading dimension below 2^24); rows past M re-read
   // the last row and their results are never stored
-  const int mlast = M - 1 - m0;
-  src.abase = A + (int64_t)m0 * lda + group * kBK;
+  const int mlast = M - 1 - om0;
+  src.abase = A + (int64_t)om0 * lda + group * kBK;
   if (PK) {
-    src.wbase = W + (int64_t)(n0 / 16) * 1024 + (int64_t)group * N * kBK;
+    src.wbase = W + (int64_t)(on0 / 16) * 1024 + (int64_t)group * N * kBK;
     src.wstep = (size_t)N * kBK;
     make_code_src<C>(src, [&](int r) { return (uint32_t)(min(r, mlast) * lda); },
                      [&](int qw, int l) { return packed_woff(qw, l, N / 16, C::BN / 16); });
   } else {
-    src.wbase = W + (int64_t)n0 * ldw + group * kBK;
+    src.wbase = W + (int64_t)on0 * ldw + group * kBK;
     src.wstep = kBK;
     make_code_src<C>(src, [&](int r) { return (uint32_t)(min(r, mlast) * lda); },
                      [&](int qw, int l) { return row_major_woff(qw, l, ldw); });
   }
   src.scale_dst = -1;
-  src.sbase = reinterpret_cast<const uint8_t*>(SA + (int64_t)m0 * nkb + group);
+  src.sbase = reinterpret_cast<const uint8_t*>(SA + (int64_t)om0 * nkb + group);
   src.soff = 0;
   if (wave < C::NS_A) {
     src.soff = (uint32_t)(min(64 * wave + lane, mlast) * nkb * 4);
     src.scale_dst = C::OFF_SA + 256 * wave;
   } else if (wave == C::NS_A) {
-    src.sbase = reinterpret_cast<const uint8_t*>(SW + (int64_t)(n0 / 128) * nkb + group);
+    src.sbase = reinterpret_cast<const uint8_t*>(SW + (int64_t)(on0 / 128) * nkb + group);
     src.soff = (uint32_t)(min(lane, (C::BN + 127) / 128 - 1) * nkb * 4);
     src.scale_dst = C::OFF_SB;
   }
@@ -1963,6 +1969,18 @@ int launch_block_gemm(const uint8_t* a, int64_t lda, const float* sa, const uint
     launch_block_any<true>(a, lda, sa, w, 0, sw, M, N, K, y, ldy, out_bf16, s);
   else
     launch_block_any<false>(a, lda, sa, w, ldw, sw, M, N, K, y, ldy, out_bf16, s);
+  return check_launch();
+}
+
+// fp8b_gemm_probe: the prefill configuration of the block GEMM (128 x 128
+// tiles, packed weights, bf16 output) with every tile reading tile (0, 0)'s
+// operands (block_gemm_kernel's TILE0).
+int launch_gemm_probe(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, int64_t M, int64_t N,
+                      int64_t K, void* y, hipStream_t s) {
+  using C = BlockCfg;
+  const int64_t tiles = (M / C::BM) * (N / C::BN);
+  hipLaunchKernelGGL((block_gemm_kernel<C, true, true, FP8B_BLOCK_MMA32 != 0, true>), dim3((unsigned)tiles),
+                     dim3(C::NT), 0, s, a, K, sa, w, 0, sw, (int)M, (int)N, (int)K, y, N);
   return check_launch();
 }
 

@@ -37,6 +37,8 @@ int launch_weight_pack(const uint8_t* w, int64_t G, int64_t N, int64_t K, int64_
 int launch_block_gemm(const uint8_t* a, int64_t lda, const float* sa, const uint8_t* w,
                       int64_t ldw, const float* sw, int64_t M, int64_t N, int64_t K, void* y,
                       int64_t ldy, int out_bf16, bool packed, hipStream_t s);
+int launch_gemm_probe(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, int64_t M, int64_t N,
+                      int64_t K, void* y, hipStream_t s);
 int launch_mx_gemm(const uint8_t* a, int64_t lda, const uint8_t* ea, const uint8_t* b,
                    int64_t ldb, const uint8_t* eb, int64_t M, int64_t N, int64_t K, float* y,
                    int64_t ldy, hipStream_t s);

@@ -487,6 +487,28 @@ typedef enum { FP8B_PROBE_COPY = 0, FP8B_PROBE_EMPTY = 1 } fp8b_probe_kind;
 int fp8b_stream_probe(int kind, const void *x, int64_t M, int64_t K,
                       uint8_t *q, float *scales, void *stream);
 
+/*
+ * fp8b_gemm_probe -- a measurement aid, not a step of the method: the
+ * kernel fp8_block_gemm_packed runs for prefill-sized problems (128 x 128
+ * tiles, bf16 output) with every workgroup reading the codes and scales of
+ * output tile (0, 0) and writing its results to its own output tile, so
+ * the operands stay resident in L2.  It does the same work per tile as the
+ * GEMM; timed beside it, it shows what the operand traffic beyond L2 costs.
+ * Tile (0, 0) of y is the GEMM's own result; the others hold copies of it.
+ *
+ *   kind      FP8B_GEMM_PROBE_TILE0.
+ *   a, a_scales, w_packed, w_scales: as for fp8_block_gemm_packed with
+ *             ld_a = K.
+ *   M, N, K   multiples of 128, each >= 128 (M <= 2^30, N < 2^24, K < 2^24,
+ *             (M/128) x (N/128) < 2^31 tiles).
+ *   y         bf16 [M][N], 16-byte aligned (ld_y = N).
+ *   Returns FP8B_EUNSUPPORTED for another kind.
+ */
+typedef enum { FP8B_GEMM_PROBE_TILE0 = 0 } fp8b_gemm_probe_kind;
+int fp8b_gemm_probe(int kind, const uint8_t *a, const float *a_scales,
+                    const uint8_t *w_packed, const float *w_scales, int64_t M,
+                    int64_t N, int64_t K, void *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
         "fp8b_abi_version", "fp8b_status_string", "fp8_act_quant", "fp8_weight_quant",
         "fp8_block_gemm", "mxfp8_gemm", "fp8_grouped_gemm", "fp8_moe_combine", "fp8_weight_dequant", "fp8_kv_quant", "fp8_kv_dequant",
         "fp8_delayed_state_init", "fp8_delayed_quant", "fp8_delayed_quant_noalloc", "fp8_cast_f32",
-        "fp8_weight_pack", "fp8_block_gemm_packed", "fp8_grouped_gemm_packed", "fp8b_mfma_loop",
+        "fp8_weight_pack", "fp8_block_gemm_packed", "fp8_grouped_gemm_packed", "fp8b_mfma_loop", "fp8b_gemm_probe",
         "fp8b_stream_probe"])
 
 
@@ -265,6 +265,25 @@ def test_stream_probe_validation(L):
     assert f(0, GOOD, 0, 256, GOOD, GOOD, NULL) == -1       # M < 1
     assert f(1, GOOD, 4, 200, GOOD, GOOD, NULL) == -1       # K % 128
     assert f(0, ODD, 4, 256, GOOD, GOOD, NULL) == -2
+
+
+def test_gemm_probe_validation(L):
+    f = L.fp8b_gemm_probe
+    args = [0, GOOD, GOOD, GOOD, GOOD, 256, 384, 512, GOOD, NULL]
+    bad = list(args); bad[0] = 1
+    assert f(*bad) == -3                                    # unknown kind
+    for i in (1, 2, 3, 4, 8):
+        bad = list(args); bad[i] = NULL
+        assert f(*bad) == -1
+    for i, v in ((5, 200), (6, 100), (7, 64), (5, 0)):      # multiples of 128, at least 128
+        bad = list(args); bad[i] = v
+        assert f(*bad) == -1
+    bad = list(args); bad[6] = 1 << 24
+    assert f(*bad) == -1                                    # N beyond 32-bit in-tile offsets
+    bad = list(args); bad[1] = ODD
+    assert f(*bad) == -2
+    bad = list(args); bad[8] = ODD
+    assert f(*bad) == -2
 
 
 def test_binding_rejects_cpu_misuse():

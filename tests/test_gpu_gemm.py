@@ -748,3 +748,23 @@ def test_register_streamed_decode_at_the_cu_count(F, orc, extra_tiles):
         oa, osa = orc.act_quant(W.bits(c.x[rows]), 128, 1)
         yr, bnd = orc.block_gemm(oa, osa, ow, osw)
         assert_parity(_np(y[rows]), yr, bnd, True, f"M {M} N {N}")
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 384, 640), (2048, 2304, 1024)])
+def test_gemm_probe_computes_tile_zero_everywhere(F, M, N, K):
+    """fp8b_gemm_probe (a measurement aid): every workgroup reads output tile
+    (0, 0)'s operands, so tile (0, 0) of its output is the packed GEMM's own
+    tile bit for bit, and every other tile is a copy of it.  Both shapes run
+    the GEMM on its plain 128 x 128 tiles (an odd K-block count; more tiles
+    than CUs), the kernel the probe runs."""
+    c = W.prefill_linear(device=DEV, M=M, K=K, N=N, seed=M + N)
+    a, sa = F.fp8_act_quant(c.x, 128, "fp32")
+    wq, ws = F.fp8_weight_quant(c.w, "fp32")
+    wp = F.fp8_weight_pack(wq)
+    y = F.fp8_block_gemm_packed(a, sa, wp, ws, torch.bfloat16)
+    yp = F.fp8b_gemm_probe(F.GEMM_PROBE_TILE0, a, sa, wp, ws)
+    torch.cuda.synchronize()
+    t0 = y[:128, :128].view(torch.int16)
+    tiles = yp.view(torch.int16).reshape(M // 128, 128, N // 128, 128).permute(0, 2, 1, 3)
+    assert torch.equal(tiles[0, 0], t0)
+    assert torch.equal(tiles, t0.expand_as(tiles))
