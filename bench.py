@@ -602,6 +602,15 @@ def run_legs(torch, F, W, dev, only=""):
                             "TFLOPs": round(2.0 * M * N * K / t / 1e12, 2),
                             "row_major_us": round(res["row_major"] * 1e6, 2),
                             "row_major_GBps": round(nbytes / res["row_major"] / 1e9, 1)}
+            if M % 128 == 0:
+                # the same tiles with every one reading tile (0, 0)'s operands
+                # (fp8b_gemm_probe): what the weight stream from HBM costs
+                wq0, ws0 = packed[0]
+                yp = torch.empty_like(y)
+                t_p = timed_graph(torch, lambda: F.fp8b_gemm_probe(F.GEMM_PROBE_TILE0, a, sa, wq0, ws0, y=yp),
+                                  iters)
+                dec[f"M{M}"]["l2_probe_us"] = round(t_p * 1e6, 2)
+                del yp
         dec["weights"] = "packed layout (fp8_weight_pack); row_major_* = the same GEMM on row-major codes"
         legs["decode"] = dec
         del copies, packed, c

@@ -1972,15 +1972,19 @@ int launch_block_gemm(const uint8_t* a, int64_t lda, const float* sa, const uint
   return check_launch();
 }
 
-// fp8b_gemm_probe: the prefill configuration of the block GEMM (128 x 128
-// tiles, packed weights, bf16 output) with every tile reading tile (0, 0)'s
-// operands (block_gemm_kernel's TILE0).
+// fp8b_gemm_probe: the 128 x 128 tile configuration fp8_block_gemm_packed
+// takes for these sizes (with its K split when the grid leaves CUs without
+// a second tile, as for 65 .. 128 tokens), bf16 output, with every tile
+// reading tile (0, 0)'s operands (block_gemm_kernel's TILE0).
 int launch_gemm_probe(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, int64_t M, int64_t N,
                       int64_t K, void* y, hipStream_t s) {
-  using C = BlockCfg;
-  const int64_t tiles = (M / C::BM) * (N / C::BN);
-  hipLaunchKernelGGL((block_gemm_kernel<C, true, true, FP8B_BLOCK_MMA32 != 0, true>), dim3((unsigned)tiles),
-                     dim3(C::NT), 0, s, a, K, sa, w, 0, sw, (int)M, (int)N, (int)K, y, N);
+  const int64_t tiles = (M / BlockCfg::BM) * (N / BlockCfg::BN);
+  if (FP8B_BLOCK_KSPLIT && tiles <= cu_count(s) && (K / kBK) % 2 == 0)
+    hipLaunchKernelGGL((block_gemm_kernel<BlockKsCfg, true, true, true, true>), dim3((unsigned)tiles),
+                       dim3(BlockKsCfg::NT), 0, s, a, K, sa, w, 0, sw, (int)M, (int)N, (int)K, y, N);
+  else
+    hipLaunchKernelGGL((block_gemm_kernel<BlockCfg, true, true, FP8B_BLOCK_MMA32 != 0, true>), dim3((unsigned)tiles),
+                       dim3(BlockCfg::NT), 0, s, a, K, sa, w, 0, sw, (int)M, (int)N, (int)K, y, N);
   return check_launch();
 }
 

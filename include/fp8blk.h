@@ -489,12 +489,14 @@ int fp8b_stream_probe(int kind, const void *x, int64_t M, int64_t K,
 
 /*
  * fp8b_gemm_probe -- a measurement aid, not a step of the method: the
- * kernel fp8_block_gemm_packed runs for prefill-sized problems (128 x 128
- * tiles, bf16 output) with every workgroup reading the codes and scales of
- * output tile (0, 0) and writing its results to its own output tile, so
- * the operands stay resident in L2.  It does the same work per tile as the
- * GEMM; timed beside it, it shows what the operand traffic beyond L2 costs.
- * Tile (0, 0) of y is the GEMM's own result; the others hold copies of it.
+ * 128 x 128 tile kernel fp8_block_gemm_packed runs for these sizes (with
+ * its K split when the grid has at most one tile per CU and the number of
+ * K blocks is even, as at 65 .. 128 tokens), bf16 output, with every
+ * workgroup reading the codes and scales of output tile (0, 0) and writing
+ * its results to its own output tile, so the operands stay resident in L2.
+ * It does the same work per tile as the GEMM; timed beside it, it shows
+ * what the operand traffic beyond L2 costs.  Tile (0, 0) of y is the
+ * GEMM's own result; the others hold copies of it.
  *
  *   kind      FP8B_GEMM_PROBE_TILE0.
  *   a, a_scales, w_packed, w_scales: as for fp8_block_gemm_packed with

@@ -750,13 +750,14 @@ def test_register_streamed_decode_at_the_cu_count(F, orc, extra_tiles):
         assert_parity(_np(y[rows]), yr, bnd, True, f"M {M} N {N}")
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 384, 640), (2048, 2304, 1024)])
+@pytest.mark.parametrize("M,N,K", [(256, 384, 640), (2048, 2304, 1024), (128, 1024, 1024)])
 def test_gemm_probe_computes_tile_zero_everywhere(F, M, N, K):
     """fp8b_gemm_probe (a measurement aid): every workgroup reads output tile
     (0, 0)'s operands, so tile (0, 0) of its output is the packed GEMM's own
-    tile bit for bit, and every other tile is a copy of it.  Both shapes run
-    the GEMM on its plain 128 x 128 tiles (an odd K-block count; more tiles
-    than CUs), the kernel the probe runs."""
+    tile bit for bit, and every other tile is a copy of it.  The first two
+    shapes run the plain 128 x 128 tiles (an odd K-block count; more tiles
+    than CUs), the third their K-split form (eight tiles, eight K blocks),
+    as the GEMM does."""
     c = W.prefill_linear(device=DEV, M=M, K=K, N=N, seed=M + N)
     a, sa = F.fp8_act_quant(c.x, 128, "fp32")
     wq, ws = F.fp8_weight_quant(c.w, "fp32")
