@@ -191,12 +191,17 @@ def _counts_case(counts, T, N, K, seed):
                      torch.from_numpy(experts.astype(np.int32)))
 
 
-@pytest.mark.parametrize("kind", ["tails", "short", "small"])
+@pytest.mark.parametrize("kind", ["tails", "short", "small", "every_count"])
 def test_grouped_packed_is_bit_identical(F, orc, kind):
     if kind == "tails":
         case = _counts_case([0, 1, 16, 17, 32, 33, 127, 128, 129, 144, 160, 161, 256, 300, 0, 5], 200, 256, 640, 41)
     elif kind == "short":
         case = _counts_case([3, 0, 31, 7, 1, 0, 20, 16], 64, 384, 1152, 43)
+    elif kind == "every_count":
+        # one expert for every row count 1 .. 161 (between two empty ones):
+        # every stream-item subtile count, every tail tile, whole tiles plus
+        # either kind of tail, in one launch
+        case = _counts_case([0] + list(range(1, 162)) + [0], 256, 128, 256, 47)
     else:
         case = W.moe_case(T=64, E=8, topk=2, N=256, K=384)
     a, sa, wq, ws, ri, offs = _moe_inputs(F, case)
@@ -206,7 +211,7 @@ def test_grouped_packed_is_bit_identical(F, orc, kind):
         y1 = F.fp8_grouped_gemm_packed(a, sa, ri, offs, wp, ws, out)
         torch.cuda.synchronize()
         _same_bits(y1, y0, f"grouped {kind} {out}")
-    if kind == "tails":   # and against the oracle directly
+    if kind in ("tails", "every_count"):   # and against the oracle directly
         E, N, K = case.w.shape
         oa, osa = orc.act_quant(W.bits(case.x), 128, 0)
         wl, sl = zip(*[orc.weight_quant(W.bits(case.w[e]), 0) for e in range(E)])
