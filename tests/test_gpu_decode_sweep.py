@@ -49,3 +49,23 @@ def test_block_gemm_every_token_count(F, orc, N, K, fmt):
             yg = y.float().cpu().numpy().astype(np.float64)
             assert yg.shape == (M, N)
             assert_parity(yg, yr[:M], bnd[:M], True, f"M={M} {name} {N}x{K} {fmt}")
+
+
+def test_mx_gemm_every_row_count(F, orc):
+    """mxfp8_gemm for every M from 1 to 260 (one to three 128-row m-tiles,
+    every ragged last tile) on the 128 x 128 tiles, N 256, K 384 (three K
+    steps), each launch on the first M rows of one quantised operand,
+    against the oracle element by element."""
+    Mmax, N, K = 260, 256, 384
+    a_bf, b_bf = W.mx_case(M=Mmax, N=N, K=K, seed=7)
+    qa, ea = F.fp8_act_quant(a_bf.to(DEV), 32, "e8m0")
+    qb, eb = F.fp8_act_quant(b_bf.to(DEV), 32, "e8m0")
+    oa, oea = orc.act_quant(W.bits(a_bf), 32, 2)
+    ob, oeb = orc.act_quant(W.bits(b_bf), 32, 2)
+    yr, bnd = orc.mx_gemm(oa, oea, ob, oeb)
+    for M in range(1, Mmax + 1):
+        y = F.mxfp8_gemm(qa[:M], ea[:M], qb, eb)
+        torch.cuda.synchronize()
+        yg = y.cpu().numpy().astype(np.float64)
+        assert yg.shape == (M, N)
+        assert_parity(yg, yr[:M], bnd[:M], False, f"mx M={M}")
