@@ -431,38 +431,46 @@ __global__ __launch_bounds__(256) void delayed_step_kernel(
 // 16-byte halves 32 bytes apart, wrote ~10% more bytes than the output and
 // took 72.2 / 21.0 us against 67.1 / 19.7 us for 18432 x 7168 weights and a
 // 32768 x 1024 cache).  Grid: x = a block of rows, y = a
-// segment of 256 * UNROLL 8-code groups of a row; a row shorter than 256
-// groups (a power-of-two count) shares its workgroup with the next rows.
+// segment of 256 * UNROLL 8-code groups of a row; rows shorter than 256
+// groups (a power-of-two count) share a workgroup, UNROLL * 256 / groups
+// of them, each lane taking one group in each of UNROLL rows.
 template <int KIND, int UNROLL>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ q, int64_t rows, int64_t cols,
                                                       int64_t ldq, const float* __restrict__ scales,
                                                       uint16_t* __restrict__ out, int64_t ldo, int row_shift) {
   const int gpr = (int)(cols / 8);  // 8-code groups per row
   const int tid = threadIdx.x;
-  int64_t row;
-  int g0;
-  if (row_shift > 0) {  // 2^row_shift rows per workgroup, gpr = 256 >> row_shift
-    row = ((int64_t)blockIdx.x << row_shift) + (tid >> (8 - row_shift));
-    g0 = tid & (gpr - 1);
+  // the lane's UNROLL groups: (row, group) pairs, all loaded before any is
+  // converted (bytes in flight per lane = 8 * UNROLL)
+  int64_t row[UNROLL];
+  int grp[UNROLL];
+  if (row_shift > 0) {  // UNROLL * 2^row_shift rows per workgroup, gpr = 256 >> row_shift
+    const int64_t r0 = ((int64_t)blockIdx.x * UNROLL << row_shift) + (tid >> (8 - row_shift));
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      row[u] = r0 + ((int64_t)u << row_shift);
+      grp[u] = tid & (gpr - 1);
+    }
   } else {
-    row = blockIdx.x;
-    g0 = (int)blockIdx.y * 256 * UNROLL + tid;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      row[u] = blockIdx.x;
+      grp[u] = (int)blockIdx.y * 256 * UNROLL + tid + 256 * u;
+    }
   }
-  if (row >= rows) return;
-  const uint8_t* qr = q + row * ldq;
-  uint16_t* orow = out + row * ldo;
   u32x2 raw[UNROLL];
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
-    const int g = g0 + 256 * u;
     raw[u] = u32x2{0u, 0u};
-    if (g < gpr) raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(qr + 8 * g));
+    if (row[u] < rows && grp[u] < gpr)
+      raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(q + row[u] * ldq + 8 * grp[u]));
   }
 #pragma unroll
   for (int u = 0; u < UNROLL; ++u) {
-    const int g = g0 + 256 * u;
-    if (g >= gpr) break;
-    const float d = KIND == 0 ? scales[(row >> 7) * (cols >> 7) + (g >> 4)] : scales[row];
+    const int64_t r = row[u];
+    const int g = grp[u];
+    if (r >= rows || g >= gpr) break;  // later pairs lie further out in the same order
+    const float d = KIND == 0 ? scales[(r >> 7) * (cols >> 7) + (g >> 4)] : scales[r];
     typedef float f2 __attribute__((ext_vector_type(2)));
     u32x4 o;
 #pragma unroll
@@ -481,7 +489,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
       o[2 * i] = __builtin_bit_cast(uint32_t, b0);
       o[2 * i + 1] = __builtin_bit_cast(uint32_t, b1);
     }
-    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(orow + 8 * g));
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + r * ldo + 8 * g));
   }
 }
 
@@ -496,7 +504,19 @@ static int launch_dequant(const uint8_t* q, int64_t rows, int64_t cols, int64_t 
   int shift = 0;
   while (shift < 7 && (gpr << (shift + 1)) <= 256 && (256 % (gpr << (shift + 1))) == 0) ++shift;
   if (shift > 0 && (gpr << shift) != 256) shift = 0;  // only exact divisors of 256 share workgroups
-  const int64_t bx = shift > 0 ? (rows + (1 << shift) - 1) >> shift : rows;
+  // Rows that share a workgroup take kDqUnroll of them per lane while that
+  // leaves at least 512 workgroups (measured on MI355X: 32768 x 1024 KV
+  // rows 19.0 -> 17.9 us, 4096 x 1024 weights 4.07 -> 3.79 us; a 1001 x 512
+  // cache, 63 workgroups, 2.36 -> 2.97 us, so small launches keep one).
+  if (shift > 0 && (rows >> shift) < 4 * 512) {
+    const int64_t bx = (rows + (1 << shift) - 1) >> shift;
+    if (bx > 0x7fffffff) return FP8B_EINVAL;  // grid limit
+    hipLaunchKernelGGL((dequant_kernel<KIND, 1>), dim3((unsigned)bx), dim3(256), 0, s, q, rows, cols, ldq, scales,
+                       out, ldo, shift);
+    return check_launch();
+  }
+  const int64_t per_wg = (int64_t)kDqUnroll << shift;  // rows per workgroup when rows share one
+  const int64_t bx = shift > 0 ? (rows + per_wg - 1) / per_wg : rows;
   const int64_t segs = shift > 0 ? 1 : (gpr + 256 * kDqUnroll - 1) / (256 * kDqUnroll);
   if (bx > 0x7fffffff || segs > 65535) return FP8B_EINVAL;  // grid limits
   hipLaunchKernelGGL((dequant_kernel<KIND, kDqUnroll>), dim3((unsigned)bx, (unsigned)segs), dim3(256), 0, s, q, rows,

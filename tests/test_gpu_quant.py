@@ -296,17 +296,32 @@ def test_kv_dequant_every_code_and_strides(F, orc):
 
 
 
-@pytest.mark.parametrize("T,D", [(77, 16), (9, 16384), (100, 1040), (3, 2048)])
+@pytest.mark.parametrize("T,D", [(77, 16), (9, 16384), (100, 1040), (3, 2048), (16421, 1024), (262151, 16)])
 def test_kv_dequant_row_grouping(F, orc, T, D):
     """Every branch of the dequant grid: many rows per workgroup with a
     partial last one (16 codes a row), a row over two segments (16384), a
-    row whose 130 groups cannot share a workgroup, one row of 256 groups."""
+    row whose 130 groups cannot share a workgroup, one row of 256 groups,
+    and shared rows in launches large enough that each lane takes one group
+    in each of four rows (1024 and 16 codes a row, partial last workgroup)."""
     rng = np.random.default_rng(T * 7 + D)
     q = rng.integers(0, 256, size=(T, D), dtype=np.uint8)
     s = np.exp(rng.uniform(-20, 20, size=T)).astype(np.float32)
     out = F.fp8_kv_dequant(torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV))
     torch.cuda.synchronize()
     _deq_check(_np(out.view(torch.int16)).view(np.uint16), orc.kv_dequant(q, s), f"kv dequant {T}x{D}")
+
+
+def test_weight_dequant_shared_rows_four_per_lane(F, orc):
+    """Weights 4224 x 1024: two 128-group rows per 256 lanes, four row pairs
+    per workgroup (the grid's folded form), every element against the
+    oracle."""
+    g = W.gen(61)
+    w = W.weights(4224, 1024, 0.02, g)
+    wq, ws = F.fp8_weight_quant(w.to(DEV), "fp32")
+    out = F.fp8_weight_dequant(wq, ws)
+    torch.cuda.synchronize()
+    _deq_check(_np(out.view(torch.int16)).view(np.uint16), orc.weight_dequant(_np(wq), _np(ws)),
+               "weight dequant 4224x1024")
 
 
 def test_weight_dequant_two_segments(F, orc):
